@@ -1,0 +1,233 @@
+"""CPU oracle for C = A * B^T -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never does, and this
+package imports nothing from it.
+
+The arithmetic lives in ``oracle.c`` (plain C, IEEE double, no fast-math, no
+FMA contraction).  This module builds it with gcc, loads it with ctypes and
+marshals numpy arrays.  ``compare`` holds the acceptance rule the parity tests
+apply to a GPU result: bit-exact for integer-valued inputs, otherwise
+``|C_gpu - C_ref| <= ulp_bf16(C_ref) + 1e-4 * S`` with ``S = |s| sum_k |a*b|``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BF16 = 0
+E4M3 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it (gcc, OpenMP)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-fno-fast-math", "-ffp-contract=off", "-fno-builtin",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, i32, vp, f64 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
+    lib.oracle_gemm.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                f64, f64, i32]
+    lib.oracle_gemm.restype = i32
+    lib.oracle_gemm_sampled.argtypes = [i32, vp, vp, i64, i64, i64, i64, i64,
+                                        vp, vp, i64, f64, f64, vp, vp, i32]
+    lib.oracle_gemm_sampled.restype = i32
+    lib.oracle_bf16_round_n.argtypes = [vp, vp, i64]
+    lib.oracle_bf16_round_n.restype = None
+    lib.oracle_e4m3_table.argtypes = [vp]
+    lib.oracle_e4m3_table.restype = None
+    lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_decode.restype = f64
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = f64
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    """Host threads to use: the affinity set, capped at 16 (one GPU's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in (BF16, "bf16"):
+        return BF16
+    if dtype in (E4M3, "fp8", "e4m3"):
+        return E4M3
+    raise ValueError("unknown dtype %r" % (dtype,))
+
+
+def _as_bits(x: np.ndarray, code: int) -> np.ndarray:
+    want = np.uint16 if code == BF16 else np.uint8
+    x = np.ascontiguousarray(x)
+    if x.dtype != want:
+        raise TypeError("expected %s bit patterns, got %s" % (want, x.dtype))
+    return x
+
+
+def gemm(dtype, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+         lda: int | None = None, ldb: int | None = None,
+         scale_a: float = 1.0, scale_b: float = 1.0, threads: int | None = None,
+         want_s: bool = True):
+    """Full oracle product.
+
+    A, B are flat or 2-D arrays of bit patterns (uint16 for bf16, uint8 for
+    e4m3) with row strides lda, ldb (elements).  Returns (C bits as an
+    (M, N) uint16 array, S as an (M, N) float64 array or None).
+    """
+    code = _dtype_code(dtype)
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    A = _as_bits(A, code)
+    B = _as_bits(B, code)
+    if M > 0 and K > 0 and A.size < (M - 1) * lda + K:
+        raise ValueError("A too small")
+    if N > 0 and K > 0 and B.size < (N - 1) * ldb + K:
+        raise ValueError("B too small")
+    C = np.zeros((M, N), dtype=np.uint16)
+    S = np.zeros((M, N), dtype=np.float64) if want_s else None
+    rc = _load().oracle_gemm(code, A.ctypes.data, B.ctypes.data, C.ctypes.data,
+                             S.ctypes.data if S is not None else None,
+                             M, N, K, lda, ldb, N, float(scale_a), float(scale_b),
+                             threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm rejected its arguments")
+    return C, S
+
+
+def gemm_sampled(dtype, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
+                 rows, cols, lda: int | None = None, ldb: int | None = None,
+                 scale_a: float = 1.0, scale_b: float = 1.0,
+                 threads: int | None = None):
+    """Oracle entries C[rows[p], cols[p]] and their magnitude sums."""
+    code = _dtype_code(dtype)
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    A = _as_bits(A, code)
+    B = _as_bits(B, code)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows/cols shape mismatch")
+    n = rows.size
+    c = np.zeros(n, dtype=np.uint16)
+    s = np.zeros(n, dtype=np.float64)
+    rc = _load().oracle_gemm_sampled(code, A.ctypes.data, B.ctypes.data, M, N, K,
+                                     lda, ldb, rows.ctypes.data, cols.ctypes.data, n,
+                                     float(scale_a), float(scale_b), c.ctypes.data,
+                                     s.ctypes.data, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm_sampled rejected its arguments")
+    return c, s
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to bf16 bit patterns (RNE, single rounding)."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.uint16)
+    _load().oracle_bf16_round_n(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
+def e4m3_table() -> np.ndarray:
+    """The 256 decoded OCP E4M3FN values (NaN for the two NaN codes)."""
+    out = np.zeros(256, dtype=np.float64)
+    _load().oracle_e4m3_table(out.ctypes.data)
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Decode bf16 bit patterns to float64 (exact)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def ulp_bf16(x) -> np.ndarray:
+    """Spacing of bf16 values in the binade of |x|: 2^(max(floor(log2|x|), -126) - 7).
+
+    For an exact power of two this is the spacing above it; ulp(0) = 2^-133.
+    """
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        _, e = np.frexp(ax)
+    E = np.where(ax > 0, e - 1, -126)
+    E = np.maximum(E, -126)
+    return np.ldexp(1.0, (E - 7).astype(np.int64))
+
+
+def compare(c_gpu_bits, c_ref_bits, S=None, exact: bool = False, rel_tol: float = 1e-4):
+    """Apply the acceptance rule; return a dict of statistics.
+
+    exact=True: bit equality with +0 and -0 treated as equal.
+    Otherwise:  |C_gpu - C_ref| <= ulp_bf16(C_ref) + rel_tol * S, and any NaN or
+    infinity in C_gpu that is not in C_ref fails.
+    """
+    g = np.asarray(c_gpu_bits, dtype=np.uint16).ravel()
+    r = np.asarray(c_ref_bits, dtype=np.uint16).ravel()
+    if g.shape != r.shape:
+        raise ValueError("shape mismatch %s vs %s" % (g.shape, r.shape))
+    gv = bf16_to_f64(g)
+    rv = bf16_to_f64(r)
+    same = (g == r) | ((gv == 0) & (rv == 0))
+    stats = {"n": int(g.size), "bit_identical_frac": float(same.mean()) if g.size else 1.0,
+             "neg_zero_gpu": int(np.sum(g == 0x8000))}
+    if exact:
+        bad = ~same
+        stats.update(violations=int(bad.sum()), ok=not bool(bad.any()))
+        if bad.any():
+            idx = int(np.flatnonzero(bad)[0])
+            stats["first_bad"] = (idx, int(g[idx]), int(r[idx]))
+        return stats
+    if S is None:
+        raise ValueError("tolerance comparison needs S")
+    S = np.asarray(S, dtype=np.float64).ravel()
+    with np.errstate(invalid="ignore"):
+        err = np.abs(gv - rv)
+    bound = ulp_bf16(rv) + rel_tol * S
+    finite_ok = np.isfinite(gv) | (~np.isfinite(rv) & (g == r))
+    ok_elem = finite_ok & ((err <= bound) | same)
+    bad = ~ok_elem
+    with np.errstate(divide="ignore", invalid="ignore"):
+        err_f = np.where(np.isfinite(err), err, np.inf)
+        ratio = np.where(same, 0.0, np.where(bound > 0, err_f / bound, np.inf))
+        rel_s = np.where(same, 0.0, np.where(S > 0, err_f / S, np.inf))
+        ulps = np.where(np.isfinite(err), np.round(err / ulp_bf16(rv)), -1)
+    hist = {}
+    u, cnt = np.unique(np.clip(ulps, -1, 8).astype(np.int64), return_counts=True)
+    for a, b in zip(u.tolist(), cnt.tolist()):
+        hist[int(a)] = int(b)
+    stats.update(violations=int(bad.sum()), ok=not bool(bad.any()),
+                 max_err_over_bound=float(ratio.max()) if g.size else 0.0,
+                 max_err_over_S=float(rel_s.max()) if g.size else 0.0,
+                 ulp_hist=hist)
+    if bad.any():
+        idx = int(np.flatnonzero(bad)[0])
+        stats["first_bad"] = (idx, int(g[idx]), int(r[idx]), float(S[idx]))
+    return stats

@@ -1,0 +1,246 @@
+/*
+ * oracle.c -- the CPU oracle for C = A * B^T.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the CPU-baseline leg of the benchmark
+ * load this file's library.  The GPU library shares no code with it: no
+ * header, table, helper or constant generator.
+ *
+ * What it computes.  The pages ("HipKittens: fast and furious AMD kernels",
+ * GeekNews summary, section "Performance results") name a GEMM kernel that is
+ * fastest "in both BF16 and FP8"; the companion page ("How to make AMD GPUs go
+ * brrr", section "Real kernel example") says its hot loop is the BF16 GEMM.
+ * Neither page writes the product out, so the oracle is the textbook
+ * definition of a matrix product with the second operand stored by rows:
+ *
+ *     C[i][j] = RNE_bf16( s * sum_{k=0..K-1} dec(A[i*lda+k]) * dec(B[j*ldb+k]) )
+ *
+ * with s = 1 for BF16 inputs and s = sA*sB for FP8 inputs.  The FP8 format is
+ * the OCP E4M3FN encoding with one fp32 scale per tensor; the pages only quote
+ * an MXFP8 peak rate and give no scaling scheme, so this is a reading, listed
+ * with the others in the design notes.
+ *
+ * Arithmetic.  Everything is in IEEE double.  Every product of two decoded
+ * bf16 (8-bit significand) or e4m3 (4-bit significand) values is exact in
+ * double; the sum is taken in ascending k from +0.0 with one rounding per add
+ * (compiled without fast-math and without FMA contraction); the scale is
+ * applied once, and the result is rounded ONCE from double to bf16 with
+ * round-to-nearest-even (no float intermediate, which would round twice).
+ *
+ * Alongside C the oracle returns S[i][j] = |s| * sum_k |dec(a)*dec(b)|, the
+ * magnitude sum that the tolerance |C_gpu - C_ref| <= ulp(C_ref) + 1e-4*S uses.
+ *
+ * Pins (tests marked "not gpu"): integer-valued inputs against an int64
+ * product, exact rational sums with fractions.Fraction on tiny shapes, an
+ * identity B, the transpose identity, the e4m3 table against torch's
+ * float8_e4m3fn, the rounding function against torch's float->bf16 cast, and
+ * hand-derived fixtures under tests/golden/.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_BF16 0
+#define ORACLE_E4M3 1
+
+/* bf16 is the top half of an IEEE binary32 word: widen and reinterpret. */
+double oracle_bf16_decode(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities;
+ * S.1111.111 is NaN; exponent field 0 encodes subnormals m * 2^-9.
+ * Largest finite value 448 = 1.75 * 2^8, smallest subnormal 2^-9.
+ */
+double oracle_e4m3_decode(uint8_t b)
+{
+    int s = b >> 7;
+    int e = (b >> 3) & 15;
+    int m = b & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/*
+ * Round a double to the nearest bf16 value, ties to even, in one step.
+ * bf16 keeps 8 significant bits (7 stored), exponent range of binary32.
+ * The quantum of the binade of |x| is 2^(max(floor(log2|x|), -126) - 7);
+ * below 2^-126 the quantum stays 2^-133 (gradual underflow).  Results of
+ * magnitude 2^128 or more are infinities; NaN maps to the quiet NaN 0x7FC0.
+ */
+uint16_t oracle_bf16_round(double x)
+{
+    int sign, e, E;
+    double ax, q, r;
+    float f;
+    uint32_t u;
+    uint16_t bits;
+
+    if (isnan(x))
+        return 0x7FC0;
+    sign = signbit(x) ? 1 : 0;
+    ax = fabs(x);
+    if (isinf(ax))
+        return sign ? 0xFF80 : 0x7F80;
+    if (ax == 0.0)
+        return sign ? 0x8000 : 0x0000;
+    frexp(ax, &e);           /* ax = f * 2^e with f in [0.5, 1) */
+    E = e - 1;               /* floor(log2 ax) */
+    if (E < -126)
+        E = -126;
+    q = ldexp(1.0, E - 7);
+    r = rint(ax / q) * q;    /* ax / q is exact; rint rounds half to even */
+    if (r >= ldexp(1.0, 128))
+        return sign ? 0xFF80 : 0x7F80;
+    f = (float)r;            /* exact: at most 8 significant bits, in range */
+    memcpy(&u, &f, sizeof u);
+    bits = (uint16_t)(u >> 16);
+    return (uint16_t)(sign ? (bits | 0x8000u) : bits);
+}
+
+static double decode_elem(int dtype, const void *base, int64_t idx,
+                          const double *e4m3_table)
+{
+    if (dtype == ORACLE_BF16)
+        return oracle_bf16_decode(((const uint16_t *)base)[idx]);
+    return e4m3_table[((const uint8_t *)base)[idx]];
+}
+
+/* One output element: the dot product in ascending k, then the scale. */
+static void dot_one(int dtype, const void *A, const void *B, int64_t i, int64_t j,
+                    int64_t K, int64_t lda, int64_t ldb, double s,
+                    const double *tab, double *c_out, double *s_out)
+{
+    double acc = 0.0, mag = 0.0;
+    int64_t k;
+    for (k = 0; k < K; ++k) {
+        double a = decode_elem(dtype, A, i * lda + k, tab);
+        double b = decode_elem(dtype, B, j * ldb + k, tab);
+        double p = a * b;
+        acc = acc + p;
+        mag = mag + fabs(p);
+    }
+    *c_out = acc * s;
+    *s_out = mag * fabs(s);
+}
+
+static int check_args(int dtype, const void *A, const void *B, int64_t M, int64_t N,
+                      int64_t K, int64_t lda, int64_t ldb)
+{
+    if (dtype != ORACLE_BF16 && dtype != ORACLE_E4M3)
+        return 1;
+    if (M < 0 || N < 0 || K < 0)
+        return 1;
+    if (K > 0 && ((M > 0 && (A == NULL || lda < K)) || (N > 0 && (B == NULL || ldb < K))))
+        return 1;
+    return 0;
+}
+
+/*
+ * Full product.  C (bf16 bits, row stride ldc) and S (double, row stride N,
+ * may be NULL) are written for 0 <= i < M, 0 <= j < N; nothing else is
+ * touched.  Returns 0 on success, 1 on invalid arguments.
+ */
+int oracle_gemm(int dtype, const void *A, const void *B, uint16_t *C, double *S,
+                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                double scale_a, double scale_b, int nthreads)
+{
+    double tab[256];
+    double s = (dtype == ORACLE_E4M3) ? scale_a * scale_b : 1.0;
+    int64_t i;
+    int t;
+
+    if (check_args(dtype, A, B, M, N, K, lda, ldb) || ldc < N || (M > 0 && N > 0 && C == NULL))
+        return 1;
+    for (t = 0; t < 256; ++t)
+        tab[t] = oracle_e4m3_decode((uint8_t)t);
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (i = 0; i < M; ++i) {
+        int64_t j;
+        for (j = 0; j < N; ++j) {
+            double c, m;
+            dot_one(dtype, A, B, i, j, K, lda, ldb, s, tab, &c, &m);
+            C[i * ldc + j] = oracle_bf16_round(c);
+            if (S)
+                S[i * N + j] = m;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Selected entries only: for p in [0, n) compute C[rows[p]][cols[p]] and its
+ * magnitude sum.  This lets full-size products be checked on a sample.
+ */
+int oracle_gemm_sampled(int dtype, const void *A, const void *B,
+                        int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                        const int64_t *rows, const int64_t *cols, int64_t n,
+                        double scale_a, double scale_b,
+                        uint16_t *c_out, double *s_out, int nthreads)
+{
+    double tab[256];
+    double s = (dtype == ORACLE_E4M3) ? scale_a * scale_b : 1.0;
+    int64_t p;
+    int t;
+
+    if (check_args(dtype, A, B, M, N, K, lda, ldb) || n < 0)
+        return 1;
+    for (p = 0; p < n; ++p)
+        if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N)
+            return 1;
+    for (t = 0; t < 256; ++t)
+        tab[t] = oracle_e4m3_decode((uint8_t)t);
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (p = 0; p < n; ++p) {
+        double c, m;
+        dot_one(dtype, A, B, rows[p], cols[p], K, lda, ldb, s, tab, &c, &m);
+        c_out[p] = oracle_bf16_round(c);
+        if (s_out)
+            s_out[p] = m;
+    }
+    return 0;
+}
+
+/* Vector forms of the scalar helpers, for the self-checks. */
+void oracle_bf16_round_n(const double *x, uint16_t *out, int64_t n)
+{
+    int64_t p;
+    for (p = 0; p < n; ++p)
+        out[p] = oracle_bf16_round(x[p]);
+}
+
+void oracle_e4m3_table(double *out256)
+{
+    int t;
+    for (t = 0; t < 256; ++t)
+        out256[t] = oracle_e4m3_decode((uint8_t)t);
+}
+
+int oracle_num_threads_available(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,72 @@
+"""The oracle's pins must be able to fail.
+
+Each case below plants one plausible mistake in a copy of oracle.c (a dropped
+term, float accumulation, a transposed operand, a wrong e4m3 bias or sign,
+rounding twice, the wrong tie rule, a lost scale, a lost subnormal clamp, an
+ignored row stride), builds the copy on the CPU in a temporary directory, and
+runs the pins of test_oracle.py against it.  At least one pin must fail for
+every mutant.  The oracle itself is never modified.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "dropped_last_term": ("for (k = 0; k < K; ++k)", "for (k = 0; k + 1 < K; ++k)"),
+    "float_accumulation": ("double acc = 0.0, mag = 0.0;", "float acc = 0.0f; double mag = 0.0;"),
+    "transposed_B": ("B, j * ldb + k", "B, k * ldb + j"),
+    "ignored_lda": ("A, i * lda + k", "A, i * K + k"),
+    "e4m3_bias_8": ("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)"),
+    "e4m3_no_sign": ("return s ? -mag : mag;", "return mag;"),
+    "e4m3_subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "double_rounding": ("r = rint(ax / q) * q;", "r = rint((double)(float)ax / q) * q;"),
+    "ties_away": ("r = rint(ax / q) * q;", "r = round(ax / q) * q;"),
+    "lost_scale": ("*c_out = acc * s;", "*c_out = acc;"),
+    "no_subnormal_clamp": ("E = -126;", "E = E;"),
+}
+
+PINS = [
+    lambda m: [pins.test_golden_fixture(m, c) for c in pins.GOLDEN_CASES],
+    pins.test_e4m3_table_matches_torch,
+    pins.test_e4m3_landmarks,
+    pins.test_bf16_round_single_rounding_cases,
+    pins.test_bf16_round_matches_torch_ties_and_edges,
+    lambda m: pins.test_integer_bf16_exact(m, 17, 9, 33, 3),
+    lambda m: pins.test_integer_fp8_exact_with_power_of_two_scales(m, 4, 4, 16),
+    lambda m: pins.test_fraction_bruteforce_bf16(m, 0),
+    lambda m: pins.test_fraction_bruteforce_fp8(m, 0),
+    pins.test_identity_B_bf16,
+    pins.test_non_square_orientation,
+    pins.test_strided_equals_packed,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(tmp_path, monkeypatch, name):
+    old, new = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(old) >= 1, "mutation anchor missing: %r" % old
+    mutant_src = tmp_path / "oracle_mutant.c"
+    mutant_src.write_text(text.replace(old, new))
+    lib_path = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                    "-ffp-contract=off", "-o", str(lib_path), str(mutant_src), "-lm"],
+                   check=True)
+    monkeypatch.setattr(oracle, "_LIB", str(lib_path))
+    monkeypatch.setattr(oracle, "_lib", None)
+    oracle._load()
+    failed = []
+    for pin in PINS:
+        try:
+            pin(oracle)
+        except (AssertionError, ValueError) as e:  # a pin fired
+            failed.append(getattr(pin, "__name__", "pin"))
+    monkeypatch.setattr(oracle, "_lib", None)
+    assert failed, "no pin caught mutant %s" % name
