@@ -1,0 +1,213 @@
+"""Benchmark: BF16 GEMM C = A * B^T at 8192^3 on one MI355X (TFLOP/s, % of 2.5 PF).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--schedule S] [--grid-order G] [--no-cpu-baseline]
+
+A step is one call of the whole path (hk_gemm_bf16 / hk_gemm_fp8 through the
+C ABI) on inputs already resident in HBM.  W untimed steps, then exactly K
+timed steps bracketed by device synchronisation; `value` is 2*M*N*K*steps /
+elapsed.  Each launch is also bracketed by HIP events on its own stream, and
+the mean event duration gives `roofline.achieved`.  The CPU baseline times the
+FP64 oracle on a bounded sample of output rows on the host cores.  Prints one
+JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_8192")
+    ap.add_argument("--schedule", default="auto")
+    ap.add_argument("--grid-order", default="auto")
+    ap.add_argument("--group-m", type=int, default=0)
+    ap.add_argument("--window", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time each launch after an L2/LLC flush and report it")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch recorded under profiles/ for this kernel source, or None.
+
+    profiles/traffic_<kernel>_<workload>.md holds 'source_sha256: X' and
+    'hbm_bytes_per_launch: Y'; the value is used only while X matches the
+    current kernel sources.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m1 = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m2 = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m1 and m2):
+        return None
+    return (m1.group(1), float(m2.group(1))) if m1.group(1) == kernel_source_sha() else None
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_gemm_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def cpu_baseline(w, x, seconds: float):
+    """The oracle, untuned, on whole output rows; scaled to TFLOP/s."""
+    import numpy as np
+    import oracle
+    import gemm_inputs
+    threads = oracle.default_threads()
+    A = gemm_inputs.bits(x["A"])
+    B = gemm_inputs.bits(x["B"])
+    dt = "bf16" if w.dtype == "bf16" else "fp8"
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.gemm(dt, A[:rows].ravel(), B.ravel(), rows, w.N, w.K,
+                    scale_a=x["scale_a"], scale_b=x["scale_b"], threads=threads, want_s=False)
+        return time.perf_counter() - t0
+
+    rows = max(1, threads // 2)
+    t = run(rows)
+    per_row = t / rows
+    rows = int(max(threads, min(w.M, seconds / max(per_row, 1e-9))))
+    rows = max(threads, (rows // threads) * threads)
+    t = run(rows)
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d output rows (all %d columns, K=%d), FP64 scalar oracle, %.1f s"
+                      % (rows, w.M, w.N, w.K, t)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only; --gpus %d is not supported (every box here has "
+              "a single MI355X, and this GEMM has no multi-GPU path)" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gemm_inputs
+    import fp8_gemm_02_amd as hk
+
+    w = gemm_inputs.WORKLOADS[a.workload]
+    print("[bench] workload %s M=%d N=%d K=%d %s" % (w.name, w.M, w.N, w.K, w.dtype),
+          file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = gemm_inputs.make_inputs(w)
+    A = x["A"].to(dev)
+    B = x["B"].to(dev)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    dtype_code = hk.HK_DTYPE_BF16 if w.dtype == "bf16" else hk.HK_DTYPE_FP8_E4M3
+    opts = dict(schedule=a.schedule, grid_order=a.grid_order, group_m=a.group_m, window=a.window)
+    plan = hk.hk_gemm_plan(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, **opts)
+    stream = torch.cuda.Stream()
+    sa, sb = x["scale_a"], x["scale_b"]
+
+    def step():
+        hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, sa, sb,
+                      stream=stream, **opts)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(a.warmup):
+            step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done (%d steps), timing %d" % (a.warmup, a.steps), file=sys.stderr,
+          flush=True)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(a.steps):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean_ms = sum(durs_ms) / len(durs_ms)
+    flops = w.flops
+    value = flops * a.steps / elapsed / 1e12
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": "GEMM TFLOP/s at BF16 8192^3 and % of 2.5 PF BF16 peak (1 MI355X)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "a_layout": "MxK row-major", "b_layout": "NxK row-major",
+                   "distribution": w.dist, "kernel": plan["kernel_name"],
+                   "schedule": plan["schedule"], "grid_order": plan["grid_order"],
+                   "group_m": plan["group_m"], "window": plan["window"]},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS[w.dtype], 2),
+        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(durs_ms[len(durs_ms) // 2], 4),
+                      "min": round(durs_ms[0], 4), "max": round(durs_ms[-1], 4)},
+    }
+    tr = traffic_from_profiles(plan["kernel_name"], w.name)
+    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
+                       "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                       "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4),
+                       "traffic": tr[1] if tr else None,
+                       "algorithmic_flops_per_launch": flops,
+                       "algorithmic_bytes_per_launch": w.algorithmic_bytes}
+
+    if a.extra:
+        # per-launch time after flushing L2 and the last-level cache
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        fl = []
+        for _ in range(max(5, a.steps // 5)):
+            flush.fill_(1)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                s.record(stream)
+                step()
+                e.record(stream)
+            torch.cuda.synchronize()
+            fl.append(s.elapsed_time(e))
+        fl.sort()
+        out["flushed_kernel_ms_median"] = round(fl[len(fl) // 2], 4)
+        del flush
+
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,210 @@
+"""Python binding of libhkgemm.so (C ABI in include/hk_gemm.h).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  Functions take device pointers as ints or torch tensors (their
+``data_ptr()``), and a stream as a HIP stream handle, a ``torch.cuda.Stream``
+or None (torch's current stream on the current device).
+
+The library must have been built (``python -m fp8_gemm_02_amd._build`` or
+``__graft_entry__.build()``); there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhkgemm.so")
+
+HK_SUCCESS = 0
+HK_ERROR_INVALID_VALUE = 1
+HK_ERROR_NOT_SUPPORTED = 2
+HK_ERROR_LAUNCH = 3
+
+HK_DTYPE_BF16 = 0
+HK_DTYPE_FP8_E4M3 = 1
+
+HK_SCHEDULE_AUTO = 0
+HK_SCHEDULE_PINGPONG8 = 1
+HK_SCHEDULE_INTERLEAVE4 = 2
+HK_SCHEDULE_BASIC = 3
+
+HK_GRID_AUTO = 0
+HK_GRID_ROW_MAJOR = 1
+HK_GRID_XCD = 2
+
+SCHEDULES = {"auto": 0, "pingpong8": 1, "interleave4": 2, "basic": 3}
+GRID_ORDERS = {"auto": 0, "row_major": 1, "xcd": 2}
+
+EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_ex", "hk_gemm_plan", "hk_grid_map",
+            "hk_status_string", "hk_version")
+
+
+class HKError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s" % (where, status_string(status)))
+
+
+class GemmOpts(ctypes.Structure):
+    _fields_ = [("schedule", ctypes.c_int32), ("grid_order", ctypes.c_int32),
+                ("group_m", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("schedule", ctypes.c_int32), ("grid_order", ctypes.c_int32),
+                ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+                ("tile_k", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+                ("workgroups", ctypes.c_int64), ("lds_bytes", ctypes.c_int32),
+                ("group_m", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("kernel_name", ctypes.c_char * 96)]
+
+    def as_dict(self):
+        d = {name: getattr(self, name) for name, _ in self._fields_ if name != "kernel_name"}
+        d["kernel_name"] = self.kernel_name.decode()
+        return d
+
+
+_lib = None
+
+
+def lib():
+    """Load libhkgemm.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libhkgemm.so is not built (%s); run python -m fp8_gemm_02_amd._build"
+                          % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    L.hk_gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+    L.hk_gemm_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, vp]
+    L.hk_gemm_ex.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
+                             ctypes.POINTER(GemmOpts), vp]
+    L.hk_gemm_plan.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                               ctypes.POINTER(GemmOpts), ctypes.POINTER(PlanInfo)]
+    L.hk_grid_map.argtypes = [i32, i64, i64, i32, i32, i32, i64, vp, vp, vp]
+    L.hk_status_string.argtypes = [i32]
+    L.hk_status_string.restype = ctypes.c_char_p
+    L.hk_version.argtypes = []
+    for name in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_ex", "hk_gemm_plan", "hk_grid_map",
+                 "hk_version"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().hk_status_string(int(status)).decode()
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s) -> int:
+    if s is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _opts(schedule=0, grid_order=0, group_m=0, window=0):
+    if isinstance(schedule, str):
+        schedule = SCHEDULES[schedule]
+    if isinstance(grid_order, str):
+        grid_order = GRID_ORDERS[grid_order]
+    o = GemmOpts()
+    o.schedule, o.grid_order, o.group_m, o.window = schedule, grid_order, group_m, window
+    return o
+
+
+def _check(status: int, where: str, raise_on_error: bool):
+    if raise_on_error and status != HK_SUCCESS:
+        raise HKError(status, where)
+    return status
+
+
+def hk_gemm_bf16(A, B, C, M, N, K, lda, ldb, ldc, stream=None, raise_on_error=True):
+    st = lib().hk_gemm_bf16(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc, _stream(stream))
+    return _check(st, "hk_gemm_bf16", raise_on_error)
+
+
+def hk_gemm_fp8(A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b, stream=None,
+                raise_on_error=True):
+    st = lib().hk_gemm_fp8(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                           float(scale_a), float(scale_b), _stream(stream))
+    return _check(st, "hk_gemm_fp8", raise_on_error)
+
+
+def hk_gemm_ex(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,
+               schedule=0, grid_order=0, group_m=0, window=0, stream=None,
+               raise_on_error=True):
+    o = _opts(schedule, grid_order, group_m, window)
+    st = lib().hk_gemm_ex(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                          float(scale_a), float(scale_b), ctypes.byref(o), _stream(stream))
+    return _check(st, "hk_gemm_ex", raise_on_error)
+
+
+def hk_gemm_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, schedule=0, grid_order=0,
+                 group_m=0, window=0):
+    """Return the launch description as a dict; raises HKError on invalid input."""
+    o = _opts(schedule, grid_order, group_m, window)
+    info = PlanInfo()
+    st = lib().hk_gemm_plan(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                            ctypes.byref(o), ctypes.byref(info))
+    _check(st, "hk_gemm_plan", True)
+    return info.as_dict()
+
+
+def hk_grid_map(grid_order, tiles_m, tiles_n, group_m, window, nxcd, wg):
+    """Map workgroup ids (sequence of ints) to (tm, tn) lists with the device's map."""
+    import numpy as np
+    if isinstance(grid_order, str):
+        grid_order = GRID_ORDERS[grid_order]
+    wg = np.ascontiguousarray(wg, dtype=np.int64)
+    tm = np.zeros_like(wg)
+    tn = np.zeros_like(wg)
+    st = lib().hk_grid_map(int(grid_order), tiles_m, tiles_n, group_m, window, nxcd, wg.size,
+                           wg.ctypes.data, tm.ctypes.data, tn.ctypes.data)
+    _check(st, "hk_grid_map", True)
+    return tm, tn
+
+
+def hk_version() -> int:
+    return int(lib().hk_version())
+
+
+def gemm_nt(A, B, scale_a=None, scale_b=None, out=None, stream=None, **opts):
+    """C = A @ B.T for 2-D torch device tensors (bf16, or uint8/float8_e4m3fn with scales).
+
+    A convenience over hk_gemm_ex: allocates C (bf16) with torch when `out` is
+    None; strides are taken from the tensors (rows must be K-contiguous).
+    """
+    import torch
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    if A.stride(1) != 1 or B.stride(1) != 1:
+        raise ValueError("A and B rows must be contiguous along K")
+    fp8 = A.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if out.stride(1) != 1:
+        raise ValueError("C rows must be contiguous")
+    dtype = HK_DTYPE_FP8_E4M3 if fp8 else HK_DTYPE_BF16
+    hk_gemm_ex(dtype, A, B, out, M, N, K, A.stride(0) if M > 1 else max(K, 1),
+               B.stride(0) if N > 1 else max(K, 1), out.stride(0) if M > 1 else max(N, 1),
+               1.0 if scale_a is None else scale_a, 1.0 if scale_b is None else scale_b,
+               stream=stream, **opts)
+    return out

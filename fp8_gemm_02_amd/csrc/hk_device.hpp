@@ -1,0 +1,114 @@
+// hk_device.hpp -- gfx950 device primitives used by the GEMM kernels.
+//
+// Vector types, buffer resources, direct HBM->LDS loads, LDS fragment reads,
+// the two matrix-core instructions, schedule fences and the bf16 store path.
+// Everything here is a thin, fixed-shape wrapper over a clang builtin; the
+// kernels decide layout and schedule.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+#define HK_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------- buffers
+//
+// A raw buffer resource: base address, size in bytes, no stride.  Loads whose
+// byte offset is at or beyond `bytes` return zero without touching memory;
+// the kernels use that to zero-fill rows past the matrix edge and (with an
+// offset of 0x80000000) K chunks past the end of a row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // dword3 0x00020000: 32-bit data format, no swizzle, raw addressing.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// One 16-byte direct load from a buffer into LDS.  Lane i of the wave writes
+// its 16 bytes to lds_wave_base + 16*i; lds_wave_base must be wave-uniform.
+__device__ __forceinline__ void load_lds_b128(__amdgpu_buffer_rsrc_t rsrc,
+                                              HK_LDS void* lds_wave_base, uint32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_wave_base, 16, voffset, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ MFMA wrappers
+//
+// 16x16x32 bf16: each lane supplies 8 bf16 of one row of the 16 x 32 "A"
+// operand and 8 of one column of the 32 x 16 "B" operand; lanes 16g..16g+15
+// hold K positions 8g..8g+7.  The result lane l holds rows 4*(l/16)+v,
+// column l%16 (v = 0..3).
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(i32x4 a, i32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 16x16x128 with both operands in OCP E4M3 (format code 0) and unit block
+// scales (E8M0 exponent 127 = 2^0): each lane supplies 32 bytes of K.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1,
+                                                    f32x4 c) {
+    const i32x8 a = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const i32x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ------------------------------------------------------ schedule control
+//
+// A workgroup barrier that the compiler may not move any instruction across.
+__device__ __forceinline__ void fenced_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4]
+// at 15:14, expcnt at 6:4, lgkmcnt at 11:8); a field at its maximum waits
+// for nothing.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+// ------------------------------------------------------------- epilogue
+//
+// Two fp32 values -> two bf16 (round to nearest even) packed in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Store four consecutive bf16 of one C row starting at column n, touching
+// only columns < N.  align is the guaranteed byte alignment of every
+// 4-column group start (8, 4 or 2).
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, int32_t n, int32_t N, f32x4 v,
+                                             int32_t align) {
+    const uint32_t lo = pack_bf16x2(v.x, v.y);
+    const uint32_t hi = pack_bf16x2(v.z, v.w);
+    if (n + 4 <= N) {
+        if (align >= 8) {
+            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+        } else if (align >= 4) {
+            reinterpret_cast<uint32_t*>(p)[0] = lo;
+            reinterpret_cast<uint32_t*>(p)[1] = hi;
+        } else {
+            p[0] = (uint16_t)lo;
+            p[1] = (uint16_t)(lo >> 16);
+            p[2] = (uint16_t)hi;
+            p[3] = (uint16_t)(hi >> 16);
+        }
+    } else {
+        if (n + 0 < N) p[0] = (uint16_t)lo;
+        if (n + 1 < N) p[1] = (uint16_t)(lo >> 16);
+        if (n + 2 < N) p[2] = (uint16_t)hi;
+    }
+}
+
+}  // namespace hk

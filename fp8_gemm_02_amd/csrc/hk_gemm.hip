@@ -1,0 +1,328 @@
+// hk_gemm.hip -- kernels and C ABI of libhkgemm.so (declared in include/hk_gemm.h).
+//
+// The host side validates arguments before any HIP call, picks a schedule
+// and a workgroup order, and enqueues exactly one kernel on the caller's
+// stream.  It allocates nothing and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "hk_gemm.h"
+#include "hk_kernels.hpp"
+
+#ifndef HK_SWZ
+#define HK_SWZ 1
+#endif
+
+#define HK_VERSION 100  // 0.1.0
+
+// ------------------------------------------------------------------ kernels
+//
+// Unmangled names so that profiler output reads as the schedule and dtype.
+
+extern "C" __global__ void __launch_bounds__(hk::kPP8Threads)
+hk_gemm_pp8_bf16(hk::GemmArgs g) {
+    __shared__ hk::i32x4 sA0[hk::kPP8StageI4], sB0[hk::kPP8StageI4];
+    __shared__ hk::i32x4 sA1[hk::kPP8StageI4], sB1[hk::kPP8StageI4];
+    hk::pp8_body<false, HK_SWZ>(g, (HK_LDS hk::i32x4*)sA0, (HK_LDS hk::i32x4*)sB0,
+                                (HK_LDS hk::i32x4*)sA1, (HK_LDS hk::i32x4*)sB1);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kPP8Threads)
+hk_gemm_pp8_fp8(hk::GemmArgs g) {
+    __shared__ hk::i32x4 sA0[hk::kPP8StageI4], sB0[hk::kPP8StageI4];
+    __shared__ hk::i32x4 sA1[hk::kPP8StageI4], sB1[hk::kPP8StageI4];
+    hk::pp8_body<true, HK_SWZ>(g, (HK_LDS hk::i32x4*)sA0, (HK_LDS hk::i32x4*)sB0,
+                               (HK_LDS hk::i32x4*)sA1, (HK_LDS hk::i32x4*)sB1);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kBasicThreads)
+hk_gemm_basic_bf16(hk::GemmArgs g) {
+    __shared__ hk::i32x4 sA[hk::kBasicStageI4], sB[hk::kBasicStageI4];
+    hk::basic_body<false>(g, (HK_LDS hk::i32x4*)sA, (HK_LDS hk::i32x4*)sB);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kBasicThreads)
+hk_gemm_basic_fp8(hk::GemmArgs g) {
+    __shared__ hk::i32x4 sA[hk::kBasicStageI4], sB[hk::kBasicStageI4];
+    hk::basic_body<true>(g, (HK_LDS hk::i32x4*)sA, (HK_LDS hk::i32x4*)sB);
+}
+
+// ------------------------------------------------------------- host side
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int32_t kDefaultGroupM = 8;
+constexpr int32_t kMI355XCUs = 256;
+constexpr int64_t kMaxRowBytes = (int64_t)1 << 31;  // strides the 32-bit offsets can address
+
+std::once_flag g_cu_once[kMaxDevices];
+int32_t g_cu_count[kMaxDevices];
+
+// Number of compute units of the current device (cached; read once per device).
+// Without a usable device, assume MI355X's 256 so that planning still works.
+int32_t current_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kMI355XCUs;
+    }
+    std::call_once(g_cu_once[dev], [dev]() {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0) {
+            (void)hipGetLastError();
+            cus = kMI355XCUs;
+        }
+        g_cu_count[dev] = cus;
+    });
+    return g_cu_count[dev];
+}
+
+struct Plan {
+    int32_t dtype;
+    int32_t schedule;
+    int32_t grid_order;
+    int32_t tile;
+    int32_t threads;
+    int32_t lds_bytes;
+    int64_t tiles_m, tiles_n;
+    hk::GemmArgs args;
+    const void* kernel;
+    const char* name;
+};
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, int64_t M,
+                   int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                   const hk_gemm_opts* opts) {
+    if (dtype != HK_DTYPE_BF16 && dtype != HK_DTYPE_FP8_E4M3) return HK_ERROR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0) return HK_ERROR_INVALID_VALUE;
+    if (opts) {
+        if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_BASIC)
+            return HK_ERROR_INVALID_VALUE;
+        if (opts->grid_order < HK_GRID_AUTO || opts->grid_order > HK_GRID_XCD)
+            return HK_ERROR_INVALID_VALUE;
+        if (opts->group_m < 0 || opts->window < 0) return HK_ERROR_INVALID_VALUE;
+        for (int i = 0; i < 4; ++i)
+            if (opts->reserved[i] != 0) return HK_ERROR_INVALID_VALUE;
+    }
+    if (M == 0 || N == 0) return HK_SUCCESS;
+    if (C == nullptr || ldc < N || !aligned(C, 2)) return HK_ERROR_INVALID_VALUE;
+    if (K > 0) {
+        if (A == nullptr || B == nullptr || lda < K || ldb < K) return HK_ERROR_INVALID_VALUE;
+        if (dtype == HK_DTYPE_BF16 && (!aligned(A, 2) || !aligned(B, 2)))
+            return HK_ERROR_INVALID_VALUE;
+    }
+    return HK_SUCCESS;
+}
+
+// Fills *p; assumes validate() passed and M, N > 0.
+hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, int64_t M,
+                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale,
+                    const hk_gemm_opts* opts, Plan* p) {
+    const int64_t esz = dtype == HK_DTYPE_BF16 ? 2 : 1;
+    if (M > INT32_MAX - 512 || N > INT32_MAX - 512 || K > INT32_MAX / 2)
+        return HK_ERROR_NOT_SUPPORTED;
+    const int64_t lda_b = (K > 0 ? lda : 0) * esz, ldb_b = (K > 0 ? ldb : 0) * esz;
+    if (lda_b >= kMaxRowBytes || ldb_b >= kMaxRowBytes) return HK_ERROR_NOT_SUPPORTED;
+
+    int32_t sched = opts ? opts->schedule : HK_SCHEDULE_AUTO;
+    int32_t order = opts ? opts->grid_order : HK_GRID_AUTO;
+    if (order == HK_GRID_AUTO) order = HK_GRID_XCD;
+
+    // Fast path: 16-byte direct loads need 16-byte aligned rows and whole
+    // 16-byte K chunks; 256 rows of stride must fit the 31-bit offsets.
+    const int64_t chunk = 16 / esz;
+    const bool fast_ok = aligned(A, 16) && aligned(B, 16) && K % chunk == 0 &&
+                         lda % chunk == 0 && ldb % chunk == 0 &&
+                         lda_b * hk::kPP8Tile < kMaxRowBytes && ldb_b * hk::kPP8Tile < kMaxRowBytes;
+    if (sched == HK_SCHEDULE_AUTO) sched = fast_ok ? HK_SCHEDULE_PINGPONG8 : HK_SCHEDULE_BASIC;
+    if (sched == HK_SCHEDULE_INTERLEAVE4) return HK_ERROR_NOT_SUPPORTED;
+    if (sched == HK_SCHEDULE_PINGPONG8 && !fast_ok) return HK_ERROR_NOT_SUPPORTED;
+
+    const bool fp8 = dtype == HK_DTYPE_FP8_E4M3;
+    if (sched == HK_SCHEDULE_PINGPONG8) {
+        p->tile = hk::kPP8Tile;
+        p->threads = hk::kPP8Threads;
+        p->lds_bytes = 4 * hk::kPP8StageI4 * 16;
+        p->kernel = fp8 ? (const void*)hk_gemm_pp8_fp8 : (const void*)hk_gemm_pp8_bf16;
+        p->name = fp8 ? "hk_gemm_pp8_fp8" : "hk_gemm_pp8_bf16";
+    } else {
+        p->tile = hk::kBasicTile;
+        p->threads = hk::kBasicThreads;
+        p->lds_bytes = 2 * hk::kBasicStageI4 * 16;
+        p->kernel = fp8 ? (const void*)hk_gemm_basic_fp8 : (const void*)hk_gemm_basic_bf16;
+        p->name = fp8 ? "hk_gemm_basic_fp8" : "hk_gemm_basic_bf16";
+    }
+    p->dtype = dtype;
+    p->schedule = sched;
+    p->grid_order = order;
+    p->tiles_m = (M + p->tile - 1) / p->tile;
+    p->tiles_n = (N + p->tile - 1) / p->tile;
+    if (p->tiles_m * p->tiles_n > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
+
+    const int32_t cus = current_cu_count();
+    hk::GemmArgs& g = p->args;
+    g.A = (const uint8_t*)A;
+    g.B = (const uint8_t*)B;
+    g.C = (uint16_t*)C;
+    g.M = (int32_t)M;
+    g.N = (int32_t)N;
+    g.K = (int32_t)K;
+    g.lda_b = (uint32_t)lda_b;
+    g.ldb_b = (uint32_t)ldb_b;
+    g.ldc = ldc;
+    g.scale = fp8 ? scale : 1.0f;
+    g.c_align = (aligned(C, 8) && ldc % 4 == 0) ? 8 : (aligned(C, 4) && ldc % 2 == 0) ? 4 : 2;
+    g.grid.order = order == HK_GRID_ROW_MAJOR ? hk::kGridRowMajor : hk::kGridXcd;
+    g.grid.tiles_m = (int32_t)p->tiles_m;
+    g.grid.tiles_n = (int32_t)p->tiles_n;
+    g.grid.group_m = (opts && opts->group_m > 0) ? opts->group_m : kDefaultGroupM;
+    g.grid.window = (opts && opts->window > 0) ? opts->window : cus;
+    g.grid.nxcd = (cus % 8 == 0) ? 8 : 1;
+    return HK_SUCCESS;
+}
+
+// C = 0 for K == 0 (the empty sum), any dtype.
+__global__ void hk_zero_c(uint16_t* C, int64_t M, int64_t N, int64_t ldc) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < M * N) C[(i / N) * ldc + i % N] = 0;
+}
+
+hk_status launch(const Plan& p, hipStream_t stream) {
+    const int64_t grid = p.tiles_m * p.tiles_n;
+    hk::GemmArgs args = p.args;
+    void* kargs[] = {&args};
+    hipError_t e = hipLaunchKernel(p.kernel, dim3((uint32_t)grid), dim3((uint32_t)p.threads),
+                                   kargs, 0, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return HK_ERROR_LAUNCH;
+    }
+    return HK_SUCCESS;
+}
+
+hk_status gemm_common(int32_t dtype, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                      int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale_a,
+                      float scale_b, const hk_gemm_opts* opts, hipStream_t stream) {
+    hk_status s = validate(dtype, A, B, C, M, N, K, lda, ldb, ldc, opts);
+    if (s != HK_SUCCESS) return s;
+    if (dtype == HK_DTYPE_FP8_E4M3 && (!isfinite(scale_a) || !isfinite(scale_b)))
+        return HK_ERROR_INVALID_VALUE;
+    if (M == 0 || N == 0) return HK_SUCCESS;
+    Plan p;
+    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a * scale_b, opts, &p);
+    if (s != HK_SUCCESS) return s;
+    if (K == 0) {
+        const int64_t total = M * N;
+        const int64_t blocks = (total + 255) / 256;
+        if (blocks > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
+        hipLaunchKernelGGL(hk_zero_c, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                           (uint16_t*)C, M, N, ldc);
+        if (hipGetLastError() != hipSuccess) return HK_ERROR_LAUNCH;
+        return HK_SUCCESS;
+    }
+    return launch(p, stream);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ C ABI
+
+extern "C" {
+
+hk_status hk_gemm_bf16(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, hk_stream_t stream) {
+    return gemm_common(HK_DTYPE_BF16, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, 1.0f, nullptr,
+                       (hipStream_t)stream);
+}
+
+hk_status hk_gemm_fp8(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc, float scale_a, float scale_b,
+                      hk_stream_t stream) {
+    return gemm_common(HK_DTYPE_FP8_E4M3, A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b,
+                       nullptr, (hipStream_t)stream);
+}
+
+hk_status hk_gemm_ex(int32_t dtype, const void* A, const void* B, void* C, int64_t M, int64_t N,
+                     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale_a,
+                     float scale_b, const hk_gemm_opts* opts, hk_stream_t stream) {
+    return gemm_common(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b, opts,
+                       (hipStream_t)stream);
+}
+
+hk_status hk_gemm_plan(int32_t dtype, const void* A, const void* B, const void* C, int64_t M,
+                       int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                       const hk_gemm_opts* opts, hk_gemm_plan_info* out) {
+    if (out == nullptr) return HK_ERROR_INVALID_VALUE;
+    hk_status s = validate(dtype, A, B, C, M, N, K, lda, ldb, ldc, opts);
+    if (s != HK_SUCCESS) return s;
+    memset(out, 0, sizeof(*out));
+    if (M == 0 || N == 0) return HK_SUCCESS;
+    Plan p;
+    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, opts, &p);
+    if (s != HK_SUCCESS) return s;
+    out->schedule = p.schedule;
+    out->grid_order = p.grid_order;
+    out->tile_m = p.tile;
+    out->tile_n = p.tile;
+    out->tile_k = hk::kRowBytes / (dtype == HK_DTYPE_BF16 ? 2 : 1);
+    out->threads = p.threads;
+    out->tiles_m = p.tiles_m;
+    out->tiles_n = p.tiles_n;
+    out->workgroups = p.tiles_m * p.tiles_n;
+    out->lds_bytes = p.lds_bytes;
+    out->group_m = p.args.grid.group_m;
+    out->window = p.args.grid.window;
+    strncpy(out->kernel_name, K == 0 ? "hk_zero_c" : p.name, sizeof(out->kernel_name) - 1);
+    return HK_SUCCESS;
+}
+
+hk_status hk_grid_map(int32_t grid_order, int64_t tiles_m, int64_t tiles_n, int32_t group_m,
+                      int32_t window, int32_t nxcd, int64_t count, const int64_t* wg,
+                      int64_t* tm, int64_t* tn) {
+    if (grid_order != HK_GRID_ROW_MAJOR && grid_order != HK_GRID_XCD)
+        return HK_ERROR_INVALID_VALUE;
+    if (tiles_m <= 0 || tiles_n <= 0 || tiles_m * tiles_n > INT32_MAX || group_m <= 0 ||
+        window <= 0 || nxcd <= 0 || count < 0)
+        return HK_ERROR_INVALID_VALUE;
+    if (count > 0 && (wg == nullptr || tm == nullptr || tn == nullptr))
+        return HK_ERROR_INVALID_VALUE;
+    const int64_t total = tiles_m * tiles_n;
+    for (int64_t i = 0; i < count; ++i)
+        if (wg[i] < 0 || wg[i] >= total) return HK_ERROR_INVALID_VALUE;
+    hk::GridParams gp;
+    gp.order = grid_order == HK_GRID_ROW_MAJOR ? hk::kGridRowMajor : hk::kGridXcd;
+    gp.tiles_m = (int32_t)tiles_m;
+    gp.tiles_n = (int32_t)tiles_n;
+    gp.group_m = group_m;
+    gp.window = window;
+    gp.nxcd = nxcd;
+    for (int64_t i = 0; i < count; ++i) {
+        uint32_t a, b;
+        hk::tile_of((uint32_t)wg[i], gp, &a, &b);
+        tm[i] = a;
+        tn[i] = b;
+    }
+    return HK_SUCCESS;
+}
+
+const char* hk_status_string(hk_status status) {
+    switch (status) {
+        case HK_SUCCESS: return "HK_SUCCESS";
+        case HK_ERROR_INVALID_VALUE: return "HK_ERROR_INVALID_VALUE";
+        case HK_ERROR_NOT_SUPPORTED: return "HK_ERROR_NOT_SUPPORTED";
+        case HK_ERROR_LAUNCH: return "HK_ERROR_LAUNCH";
+    }
+    return "HK_UNKNOWN_STATUS";
+}
+
+int32_t hk_version(void) { return HK_VERSION; }
+
+}  // extern "C"

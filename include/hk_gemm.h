@@ -1,0 +1,173 @@
+/*
+ * hk_gemm.h -- C ABI of libhkgemm.so: dense C = A * B^T on one MI355X (gfx950).
+ *
+ * The operation.  The GeekNews summary "HipKittens: fast and furious AMD
+ * kernels" (section "Performance results") reports a GEMM kernel that is the
+ * fastest in BF16 and in FP8; its companion "How to make AMD GPUs go brrr"
+ * (section "Real kernel example") shows the BF16 GEMM hot loop.  Neither page
+ * gives an interface, so this one is ours:
+ *
+ *     C[i*ldc + j] = bf16_rne( s * sum_{k<K} A[i*lda + k] * B[j*ldb + k] )
+ *
+ * for 0 <= i < M, 0 <= j < N, with FP32 accumulation.  A is M x K and B is
+ * N x K, both row-major with K contiguous (so B is used transposed), C is
+ * M x N row-major.  s = 1 for BF16 inputs, s = scale_a * scale_b for FP8.
+ *
+ * Element types.  BF16: 16-bit bfloat16 bit patterns.  FP8: OCP E4M3FN bytes
+ * (bias 7, largest finite 448, S.1111.111 is NaN), one fp32 scale per tensor
+ * passed by value.  The pages quote only an MXFP8 peak rate and no scaling
+ * scheme; per-tensor scales are the plainest reading.  C is always bf16,
+ * rounded to nearest even from the fp32 accumulator (times s for FP8).
+ *
+ * Ownership and ordering.  All pointers are device pointers owned by the
+ * caller; the library never allocates or frees memory.  Every call only
+ * enqueues work on `stream` (0 = the null stream) and returns; it never
+ * synchronises.  Buffers must stay valid until that work has completed.
+ * Calls are thread-safe; the library keeps only a per-device property cache.
+ *
+ * Errors.  Every function returns an hk_status and never aborts or throws.
+ * Arguments are validated before any HIP call; invalid ones return
+ * HK_ERROR_INVALID_VALUE and enqueue nothing: negative M, N or K; a NULL
+ * pointer for an operand that would be read or written; lda < K or ldb < K
+ * (when K > 0); ldc < N; an unknown dtype, schedule or grid order; a
+ * non-finite scale.  M == 0 or N == 0 is a no-op success.  K == 0 writes
+ * zeros to C (the empty sum is +0).  A failure reported by the HIP runtime at
+ * launch returns HK_ERROR_LAUNCH.  HK_ERROR_NOT_SUPPORTED is returned when an
+ * explicitly requested schedule cannot run the given shape or alignment
+ * (the automatic choice never returns it).
+ */
+#ifndef HK_GEMM_H
+#define HK_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; 0 selects the null stream. */
+typedef struct ihipStream_t *hk_stream_t;
+
+typedef enum hk_status {
+    HK_SUCCESS = 0,
+    HK_ERROR_INVALID_VALUE = 1,
+    HK_ERROR_NOT_SUPPORTED = 2,
+    HK_ERROR_LAUNCH = 3
+} hk_status;
+
+typedef enum hk_dtype {
+    HK_DTYPE_BF16 = 0,
+    HK_DTYPE_FP8_E4M3 = 1
+} hk_dtype;
+
+/*
+ * Intra-CU schedule ("How to make AMD GPUs go brrr", section "Intra-processor
+ * scheduling: wave patterns"):
+ *   PINGPONG8   8 waves per CU in two groups of four; while one group issues
+ *               its matrix-core cluster the other issues its memory cluster,
+ *               and they swap at workgroup barriers;
+ *   INTERLEAVE4 4 waves per CU, each interleaving its own loads with its
+ *               matrix-core instructions;
+ *   BASIC       a plain LDS-staged kernel with no alignment requirements,
+ *               used for shapes or strides the fast schedules do not accept.
+ * AUTO picks PINGPONG8 when the fast-path conditions hold, else BASIC.
+ */
+typedef enum hk_schedule {
+    HK_SCHEDULE_AUTO = 0,
+    HK_SCHEDULE_PINGPONG8 = 1,
+    HK_SCHEDULE_INTERLEAVE4 = 2,
+    HK_SCHEDULE_BASIC = 3
+} hk_schedule;
+
+/*
+ * Workgroup-to-tile order ("How to make AMD GPUs go brrr", section
+ * "Inter-processor scheduling: chiplet-aware approach"): the hardware deals
+ * workgroups to the 8 chiplets (XCDs) round-robin, so the order decides what
+ * each chiplet's L2 and the shared last-level cache can reuse.
+ *   ROW_MAJOR  workgroup w computes tile (w / tiles_n, w % tiles_n);
+ *   XCD        within each window of co-resident workgroups, the ones dealt
+ *              to one chiplet get a compact block of output tiles, and the
+ *              window as a whole covers a compact region (grouped order of
+ *              group_m tile rows).
+ * AUTO is XCD.
+ */
+typedef enum hk_grid_order {
+    HK_GRID_AUTO = 0,
+    HK_GRID_ROW_MAJOR = 1,
+    HK_GRID_XCD = 2
+} hk_grid_order;
+
+/* Optional knobs for hk_gemm_ex.  Zero-initialise for the defaults. */
+typedef struct hk_gemm_opts {
+    int32_t schedule;    /* hk_schedule */
+    int32_t grid_order;  /* hk_grid_order */
+    int32_t group_m;     /* tile rows per group in the XCD order; 0 = default */
+    int32_t window;      /* co-resident workgroups per window; 0 = CU count */
+    int32_t reserved[4]; /* must be zero */
+} hk_gemm_opts;
+
+/* What a call with these arguments would launch (filled by hk_gemm_plan). */
+typedef struct hk_gemm_plan_info {
+    int32_t schedule;      /* the schedule actually used */
+    int32_t grid_order;    /* the order actually used */
+    int32_t tile_m, tile_n, tile_k;  /* tile_k in elements */
+    int32_t threads;       /* threads per workgroup */
+    int64_t tiles_m, tiles_n;
+    int64_t workgroups;    /* 1-D grid size */
+    int32_t lds_bytes;
+    int32_t group_m, window;
+    char kernel_name[96];  /* device symbol, as profilers print it */
+} hk_gemm_plan_info;
+
+/* BF16 x BF16 -> BF16 (fp32 accumulate).  Default schedule and grid order. */
+hk_status hk_gemm_bf16(const void *A, const void *B, void *C,
+                       int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc,
+                       hk_stream_t stream);
+
+/* E4M3FN x E4M3FN -> BF16, C = scale_a * scale_b * (A * B^T). */
+hk_status hk_gemm_fp8(const void *A, const void *B, void *C,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc,
+                      float scale_a, float scale_b,
+                      hk_stream_t stream);
+
+/* Either dtype with explicit options (opts may be NULL = defaults).
+ * scale_a and scale_b are ignored for BF16. */
+hk_status hk_gemm_ex(int32_t dtype,
+                     const void *A, const void *B, void *C,
+                     int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc,
+                     float scale_a, float scale_b,
+                     const hk_gemm_opts *opts, hk_stream_t stream);
+
+/* Describe the launch hk_gemm_ex would make, without touching the GPU
+ * beyond reading (once) the current device's CU count.  Pointers only
+ * matter for their alignment and may be any value.  Returns the same
+ * validation errors as hk_gemm_ex. */
+hk_status hk_gemm_plan(int32_t dtype, const void *A, const void *B, const void *C,
+                       int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc,
+                       const hk_gemm_opts *opts, hk_gemm_plan_info *out);
+
+/* Host evaluation of the workgroup-to-tile map used on the device (the
+ * same code), for tests and locality models.  For each p < count, maps
+ * workgroup id wg[p] of a tiles_m x tiles_n grid to (tm[p], tn[p]).
+ * nxcd is the number of chiplets workgroups are dealt over (8 on MI355X).
+ * Returns HK_ERROR_INVALID_VALUE for ids outside [0, tiles_m*tiles_n) or
+ * non-positive parameters. */
+hk_status hk_grid_map(int32_t grid_order, int64_t tiles_m, int64_t tiles_n,
+                      int32_t group_m, int32_t window, int32_t nxcd,
+                      int64_t count, const int64_t *wg, int64_t *tm, int64_t *tn);
+
+/* Static string for a status code ("HK_SUCCESS", ...). */
+const char *hk_status_string(hk_status status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t hk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HK_GEMM_H */

@@ -1,0 +1,180 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+validates arguments before touching the GPU, and plans launches.
+
+No test here computes anything on a GPU; calls that would launch use fake
+pointers only where validation is expected to reject them first, or (without
+a GPU) where the launch itself must fail cleanly with HK_ERROR_LAUNCH.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_gemm_02_amd as hk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hk_gemm.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced in these tests
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hk_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return hk.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_ex", "hk_gemm_plan", "hk_grid_map",
+              "hk_status_string", "hk_version"):
+        assert n in names
+    assert set(names) == set(hk.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in _declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert hk.status_string(0) == "HK_SUCCESS"
+    assert hk.status_string(1) == "HK_ERROR_INVALID_VALUE"
+    assert hk.status_string(2) == "HK_ERROR_NOT_SUPPORTED"
+    assert hk.status_string(3) == "HK_ERROR_LAUNCH"
+    assert hk.status_string(99) == "HK_UNKNOWN_STATUS"
+    assert hk.hk_version() >= 100
+
+
+BAD_BF16 = [
+    dict(M=-1), dict(N=-1), dict(K=-1),
+    dict(A=0), dict(B=0), dict(C=0),
+    dict(lda=63), dict(ldb=63), dict(ldc=31),
+    dict(C=FAKE + 1),          # C must be 2-byte aligned
+    dict(A=FAKE + 1),          # bf16 operands must be 2-byte aligned
+]
+
+
+@pytest.mark.parametrize("bad", BAD_BF16, ids=[",".join(b) for b in BAD_BF16])
+def test_invalid_arguments_rejected_before_any_hip_call(L, bad):
+    a = dict(A=FAKE, B=FAKE, C=FAKE, M=32, N=32, K=64, lda=64, ldb=64, ldc=32)
+    a.update(bad)
+    st = L.hk_gemm_bf16(a["A"], a["B"], a["C"], a["M"], a["N"], a["K"], a["lda"], a["ldb"],
+                        a["ldc"], None)
+    assert st == hk.HK_ERROR_INVALID_VALUE
+
+
+def test_fp8_rejects_non_finite_scales(L):
+    for sa, sb in [(float("nan"), 1.0), (1.0, float("inf"))]:
+        st = L.hk_gemm_fp8(FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, sa, sb, None)
+        assert st == hk.HK_ERROR_INVALID_VALUE
+
+
+def test_ex_rejects_bad_dtype_and_options(L):
+    st = L.hk_gemm_ex(7, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0, None, None)
+    assert st == hk.HK_ERROR_INVALID_VALUE
+    for field, val in [("schedule", 9), ("grid_order", 5), ("group_m", -1), ("window", -2)]:
+        o = hk.GemmOpts()
+        setattr(o, field, val)
+        st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
+                          ctypes.byref(o), None)
+        assert st == hk.HK_ERROR_INVALID_VALUE, field
+    o = hk.GemmOpts()
+    o.reserved[2] = 1
+    st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0, ctypes.byref(o), None)
+    assert st == hk.HK_ERROR_INVALID_VALUE
+
+
+def test_empty_output_is_a_noop_success(L):
+    # M == 0 or N == 0: nothing is read or written, null pointers allowed
+    assert L.hk_gemm_bf16(0, 0, 0, 0, 16, 16, 16, 16, 16, None) == hk.HK_SUCCESS
+    assert L.hk_gemm_bf16(0, 0, 0, 16, 0, 16, 16, 16, 16, None) == hk.HK_SUCCESS
+    assert L.hk_gemm_fp8(0, 0, 0, 0, 0, 0, 0, 0, 0, 1.0, 1.0, None) == hk.HK_SUCCESS
+
+
+def test_explicit_fast_schedule_needs_alignment(L):
+    o = hk.GemmOpts()
+    o.schedule = hk.HK_SCHEDULE_PINGPONG8
+    # K not a multiple of 8 bf16 elements: the fast schedule cannot run it
+    st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 64, 64, 60, 60, 60, 64, 1.0, 1.0, ctypes.byref(o), None)
+    assert st == hk.HK_ERROR_NOT_SUPPORTED
+    # misaligned A pointer
+    st = L.hk_gemm_ex(0, FAKE + 2, FAKE, FAKE, 64, 64, 64, 64, 64, 64, 1.0, 1.0,
+                      ctypes.byref(o), None)
+    assert st == hk.HK_ERROR_NOT_SUPPORTED
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-GPU launch path")
+def test_valid_call_without_gpu_reports_launch_error(L):
+    st = L.hk_gemm_bf16(FAKE, FAKE, FAKE, 256, 256, 256, 256, 256, 256, None)
+    assert st == hk.HK_ERROR_LAUNCH
+    st = L.hk_gemm_fp8(FAKE, FAKE, FAKE, 256, 256, 256, 256, 256, 256, 0.5, 2.0, None)
+    assert st == hk.HK_ERROR_LAUNCH
+
+
+# ------------------------------------------------------------------- planning
+
+def _plan(dtype, M, N, K, lda=None, ldb=None, ldc=None, A=FAKE, B=FAKE, C=FAKE, **kw):
+    return hk.hk_gemm_plan(dtype, A, B, C, M, N, K, lda or K, ldb or K, ldc or N, **kw)
+
+
+@pytest.mark.parametrize("M,N,K,tiles", [(256, 256, 256, (1, 1)), (4096, 4096, 4096, (16, 16)),
+                                         (8192, 8192, 8192, (32, 32)),
+                                         (8192, 28672, 8192, (32, 112)),
+                                         (8191, 28670, 8200, (32, 112))])
+def test_plan_fast_path_for_every_workload(M, N, K, tiles):
+    p = _plan(hk.HK_DTYPE_BF16, M, N, K)
+    assert p["schedule"] == hk.HK_SCHEDULE_PINGPONG8
+    assert p["kernel_name"] == "hk_gemm_pp8_bf16"
+    assert (p["tiles_m"], p["tiles_n"]) == tiles
+    assert p["workgroups"] == tiles[0] * tiles[1]
+    assert p["threads"] == 512 and p["lds_bytes"] == 131072
+    assert p["tile_k"] == 64
+    assert p["grid_order"] == hk.HK_GRID_XCD
+
+
+def test_plan_fp8():
+    p = _plan(hk.HK_DTYPE_FP8_E4M3, 8192, 8192, 8192)
+    assert p["kernel_name"] == "hk_gemm_pp8_fp8" and p["tile_k"] == 128
+
+
+@pytest.mark.parametrize("K,lda,Aoff", [(60, 60, 0), (64, 66, 0), (64, 64, 2)])
+def test_plan_falls_back_to_basic(K, lda, Aoff):
+    p = _plan(hk.HK_DTYPE_BF16, 100, 100, K, lda=lda, A=FAKE + Aoff)
+    assert p["schedule"] == hk.HK_SCHEDULE_BASIC
+    assert p["kernel_name"] == "hk_gemm_basic_bf16"
+    assert (p["tiles_m"], p["tiles_n"]) == (2, 2)
+
+
+def test_plan_fp8_fast_path_needs_16_byte_k():
+    assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 8, lda=16, ldb=16)["schedule"] == hk.HK_SCHEDULE_BASIC
+    assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 32)["schedule"] == hk.HK_SCHEDULE_PINGPONG8
+
+
+def test_plan_zero_k_uses_the_fill_kernel():
+    assert _plan(hk.HK_DTYPE_BF16, 8, 8, 0, lda=1, ldb=1)["kernel_name"] == "hk_zero_c"
+
+
+def test_plan_options_are_honoured():
+    p = _plan(hk.HK_DTYPE_BF16, 4096, 4096, 4096, grid_order="row_major", group_m=4, window=128)
+    assert p["grid_order"] == hk.HK_GRID_ROW_MAJOR and p["group_m"] == 4 and p["window"] == 128
+
+
+def test_plan_rejects_huge_strides():
+    with pytest.raises(hk.HKError) as e:
+        _plan(hk.HK_DTYPE_BF16, 8, 8, 8, lda=2 ** 30, ldb=8)
+    assert e.value.status == hk.HK_ERROR_NOT_SUPPORTED

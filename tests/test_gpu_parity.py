@@ -1,0 +1,320 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Acceptance rule (element by element): bit-exact for integer-valued inputs;
+otherwise |C_gpu - C_ref| <= ulp_bf16(C_ref) + 1e-4 * S with S = |s| sum|a*b|.
+
+* Small and medium shapes (several 256-tiles plus ragged edges and a K tail)
+  are compared in full.
+* Every workload at its full size runs in the launch configuration the
+  benchmark times (hk_gemm_bf16 / hk_gemm_fp8 defaults) and is compared on a
+  sample of entries that the oracle computes one by one (random entries plus
+  the corners of every edge tile), and through properties that hold at any
+  size: integer-valued inputs (bit-exact sample), identity-like B (C equals
+  A exactly), a K-tail probe, and guard bands around C.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_gemm_02_amd as hk
+import gemm_inputs
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+RTOL = 1e-4
+SENTINEL = 0x7BAD  # a finite bf16 bit pattern no product here produces by chance
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    hk.lib()
+    torch.cuda.set_device(0)
+    return torch.device("cuda:0")
+
+
+def _bits16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _run(dtype, A, B, M, N, K, lda, ldb, ldc, sa=1.0, sb=1.0, C=None, stream=None, **opts):
+    """Launch through the C ABI on device tensors; returns C (bf16, rows of ldc)."""
+    if C is None:
+        C = torch.full((max(M, 1), ldc), 0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    if opts:
+        hk.hk_gemm_ex(dtype, A, B, C, M, N, K, lda, ldb, ldc, sa, sb, stream=stream, **opts)
+    elif dtype == hk.HK_DTYPE_BF16:
+        hk.hk_gemm_bf16(A, B, C, M, N, K, lda, ldb, ldc, stream=stream)
+    else:
+        hk.hk_gemm_fp8(A, B, C, M, N, K, lda, ldb, ldc, sa, sb, stream=stream)
+    torch.cuda.synchronize()
+    return C
+
+
+def _bf16(rows, cols, dist, seed):
+    return gemm_inputs.bf16_matrix(rows, cols, dist, seed)
+
+
+def _full_check(dtype, A_cpu, B_cpu, M, N, K, lda, ldb, exact, sa=1.0, sb=1.0, ldc=None, **opts):
+    ldc = ldc or N
+    dt = hk.HK_DTYPE_BF16 if dtype == "bf16" else hk.HK_DTYPE_FP8_E4M3
+    A = A_cpu.cuda()
+    B = B_cpu.cuda()
+    C = _run(dt, A, B, M, N, K, lda, ldb, ldc, sa, sb, **opts)
+    got = _bits16(C)[:M, :N]
+    ref, S = oracle.gemm(dtype, gemm_inputs.bits(A_cpu).ravel(), gemm_inputs.bits(B_cpu).ravel(),
+                         M, N, K, lda=lda, ldb=ldb, scale_a=sa, scale_b=sb)
+    st = oracle.compare(got, ref, S, exact=exact, rel_tol=RTOL)
+    _say(dtype, (M, N, K), "exact" if exact else "tol", opts or "", {k: st[k] for k in st
+                                                                  if k != "ulp_hist"})
+    assert st["ok"], st
+    return st
+
+
+# ------------------------------------------------------------ full compares
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_bf16_256_full(integer):
+    w = gemm_inputs.WORKLOADS["bf16_256"]
+    x = gemm_inputs.make_inputs(w, integer=integer)
+    _full_check("bf16", x["A"], x["B"], 256, 256, 256, 256, 256, exact=integer)
+
+
+@pytest.mark.parametrize("M,N,K", [(600, 700, 520), (257, 513, 136), (1, 1, 8), (17, 3, 64),
+                                   (300, 260, 8), (64, 1000, 1288)])
+@pytest.mark.parametrize("integer", [False, True])
+def test_bf16_ragged_full(M, N, K, integer):
+    dist = "int4" if integer else "uniform"
+    A = _bf16(M, K, dist, M + K)
+    B = _bf16(N, K, dist, N + K + 1)
+    _full_check("bf16", A, B, M, N, K, K, K, exact=integer)
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 600, 640), (256, 256, 256), (300, 1, 144), (33, 513, 16)])
+@pytest.mark.parametrize("integer", [False, True])
+def test_fp8_ragged_full(M, N, K, integer):
+    A, sa = gemm_inputs.fp8_matrix(M, K, 3 * M + K, integer)
+    B, sb = gemm_inputs.fp8_matrix(N, K, 5 * N + K, integer)
+    if integer:
+        sa, sb = 0.5, 4.0  # powers of two keep the scaled integer sums exact
+    _full_check("fp8", A, B, M, N, K, K, K, exact=integer, sa=sa, sb=sb)
+
+
+@pytest.mark.parametrize("schedule", ["pingpong8", "basic"])
+@pytest.mark.parametrize("grid_order", ["row_major", "xcd"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_every_variant(schedule, grid_order, dtype):
+    M, N, K = 777, 1029, 512
+    if dtype == "bf16":
+        A, B, sa, sb = _bf16(M, K, "normal", 11), _bf16(N, K, "normal", 12), 1.0, 1.0
+    else:
+        A, sa = gemm_inputs.fp8_matrix(M, K, 13)
+        B, sb = gemm_inputs.fp8_matrix(N, K, 14)
+    _full_check(dtype, A, B, M, N, K, K, K, exact=False, sa=sa, sb=sb, schedule=schedule,
+                grid_order=grid_order)
+
+
+@pytest.mark.parametrize("group_m,window", [(1, 256), (3, 100), (16, 64), (8, 7)])
+def test_grid_parameters(group_m, window):
+    M, N, K = 1300, 1100, 256
+    A = _bf16(M, K, "int4", 21)
+    B = _bf16(N, K, "int4", 22)
+    _full_check("bf16", A, B, M, N, K, K, K, exact=True, group_m=group_m, window=window)
+
+
+def test_padded_strides_and_guard_bands():
+    M, N, K, pad = 517, 300, 264, 8
+    lda, ldb, ldc = K + pad, K + 2 * pad, N + pad
+    A = _bf16(M, lda, "uniform", 31)
+    B = _bf16(N, ldb, "uniform", 32)
+    # poison the padding: a kernel that reads it gets a visibly wrong answer
+    A[:, K:] = float("nan")
+    B[:, K:] = float("nan")
+    guard = 3
+    Cbuf = torch.full(((M + 2 * guard) * ldc,), SENTINEL, dtype=torch.int16,
+                      device="cuda").view(torch.bfloat16)
+    Cv = Cbuf[guard * ldc:]
+    _run(hk.HK_DTYPE_BF16, A.cuda(), B.cuda(), M, N, K, lda, ldb, ldc, C=Cv)
+    allb = _bits16(Cbuf).reshape(M + 2 * guard, ldc)
+    assert (allb[:guard] == SENTINEL).all() and (allb[guard + M:] == SENTINEL).all()
+    body = allb[guard:guard + M]
+    assert (body[:, N:] == SENTINEL).all()
+    ref, S = oracle.gemm("bf16", gemm_inputs.bits(A).ravel(), gemm_inputs.bits(B).ravel(),
+                         M, N, K, lda=lda, ldb=ldb)
+    st = oracle.compare(body[:, :N], ref, S, rel_tol=RTOL)
+    assert st["ok"], st
+
+
+def test_misaligned_pointers_use_the_fallback():
+    M, N, K = 130, 70, 77  # odd K: no 16-byte chunks
+    A = _bf16(M, K + 1, "int4", 41)
+    B = _bf16(N, K + 1, "int4", 42)
+    Ad, Bd = A.cuda(), B.cuda()
+    C = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    # pointers offset by one element (2 bytes) and odd row strides
+    p = hk.hk_gemm_plan(0, Ad.data_ptr() + 2, Bd.data_ptr() + 2, C, M, N, K, K + 1, K + 1, N)
+    assert p["schedule"] == hk.HK_SCHEDULE_BASIC
+    hk.hk_gemm_bf16(Ad.data_ptr() + 2, Bd.data_ptr() + 2, C, M, N, K, K + 1, K + 1, N)
+    torch.cuda.synchronize()
+    a = gemm_inputs.bits(A)[:, 1:].copy()
+    b = gemm_inputs.bits(B)[:, 1:].copy()
+    ref, _ = oracle.gemm("bf16", a.ravel(), b.ravel(), M, N, K)
+    assert oracle.compare(_bits16(C), ref, exact=True)["ok"]
+
+
+def test_odd_ldc_two_byte_stores():
+    M, N, K = 70, 45, 64
+    ldc = 47
+    A = _bf16(M, K, "int4", 51)
+    B = _bf16(N, K, "int4", 52)
+    C = torch.full((M * ldc,), SENTINEL, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    _run(hk.HK_DTYPE_BF16, A.cuda(), B.cuda(), M, N, K, K, K, ldc, C=C)
+    allb = _bits16(C).reshape(M, ldc)
+    assert (allb[:, N:] == SENTINEL).all()
+    ref, _ = oracle.gemm("bf16", gemm_inputs.bits(A).ravel(), gemm_inputs.bits(B).ravel(), M, N, K)
+    assert oracle.compare(allb[:, :N], ref, exact=True)["ok"]
+
+
+def test_zero_k_writes_zeros_and_empty_is_noop():
+    C = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
+    hk.hk_gemm_bf16(0, 0, C, 5, 7, 0, 1, 1, 7)
+    torch.cuda.synchronize()
+    assert (C.float() == 0).all()
+    D = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
+    hk.hk_gemm_bf16(0, 0, D, 0, 7, 16, 16, 16, 7)
+    hk.hk_gemm_fp8(0, 0, D, 5, 0, 16, 16, 16, 7, 1.0, 1.0)
+    torch.cuda.synchronize()
+    assert (D.float() == 3).all()
+
+
+def test_non_default_stream():
+    M, N, K = 512, 384, 320
+    A = _bf16(M, K, "int4", 61).cuda()
+    B = _bf16(N, K, "int4", 62).cuda()
+    s = torch.cuda.Stream()
+    C = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    with torch.cuda.stream(s):
+        hk.hk_gemm_bf16(A, B, C, M, N, K, K, K, N, stream=s)
+    s.synchronize()
+    ref, _ = oracle.gemm("bf16", _bits16(A).ravel(), _bits16(B).ravel(), M, N, K)
+    assert oracle.compare(_bits16(C), ref, exact=True)["ok"]
+
+
+def test_repeatable_bitwise():
+    M, N, K = 1024, 768, 1024
+    A = _bf16(M, K, "normal", 71).cuda()
+    B = _bf16(N, K, "normal", 72).cuda()
+    C1 = _run(hk.HK_DTYPE_BF16, A, B, M, N, K, K, K, N)
+    C2 = _run(hk.HK_DTYPE_BF16, A, B, M, N, K, K, K, N)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+# -------------------------------------------------------- full-size workloads
+
+def _edge_samples(M, N, tile, rng, n_random):
+    """Random entries plus the four corners of every tile row/column edge."""
+    rows = [rng.integers(0, M, n_random)]
+    cols = [rng.integers(0, N, n_random)]
+    tm = np.arange(0, M, tile)
+    tn = np.arange(0, N, tile)
+    for r in np.unique(np.concatenate([tm, np.minimum(tm + tile - 1, M - 1)])):
+        for c in (0, N - 1, rng.integers(0, N)):
+            rows.append([r]); cols.append([c])
+    for c in np.unique(np.concatenate([tn, np.minimum(tn + tile - 1, N - 1)])):
+        for r in (0, M - 1, rng.integers(0, M)):
+            rows.append([r]); cols.append([c])
+    return np.concatenate(rows).astype(np.int64), np.concatenate(cols).astype(np.int64)
+
+
+def _sampled_check(w, x, integer, n_random=3000):
+    M, N, K = w.M, w.N, w.K
+    dt = hk.HK_DTYPE_BF16 if w.dtype == "bf16" else hk.HK_DTYPE_FP8_E4M3
+    sa, sb = x["scale_a"], x["scale_b"]
+    if integer and w.dtype == "fp8":
+        sa, sb = 0.5, 4.0
+    A, B = x["A"].cuda(), x["B"].cuda()
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _say("launch", w.name, "integer" if integer else w.dist, (M, N, K))
+    if dt == hk.HK_DTYPE_BF16:
+        hk.hk_gemm_bf16(A, B, C, M, N, K, K, K, N)
+    else:
+        hk.hk_gemm_fp8(A, B, C, M, N, K, K, K, N, sa, sb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.index * 7 + int(integer))
+    rows, cols = _edge_samples(M, N, 256, rng, n_random)
+    got = _bits16(C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()])
+    ref, S = oracle.gemm_sampled(w.dtype, gemm_inputs.bits(x["A"]).ravel(),
+                                 gemm_inputs.bits(x["B"]).ravel(), M, N, K, rows, cols,
+                                 scale_a=sa, scale_b=sb)
+    st = oracle.compare(got, ref, S, exact=integer, rel_tol=RTOL)
+    _say(w.name, "sampled", rows.size, {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
+    return C
+
+
+FULL = ["bf16_4096", "bf16_8192", "bf16_mlp", "bf16_mlp_ragged", "fp8_8192"]
+
+
+@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("integer", [False, True])
+def test_full_size_sampled(name, integer):
+    w = gemm_inputs.WORKLOADS[name]
+    x = gemm_inputs.make_inputs(w, integer=integer)
+    _sampled_check(w, x, integer)
+
+
+@pytest.mark.parametrize("name", ["bf16_8192", "bf16_mlp_ragged", "fp8_8192"])
+def test_full_size_identity_like_B(name):
+    """B[j, k] = 1 if j == k else 0 (j < min(N, K)): C[:, :min(N,K)] == A exactly."""
+    w = gemm_inputs.WORKLOADS[name]
+    M, N, K = w.M, w.N, w.K
+    sa_seed, _ = w.seeds()
+    if w.dtype == "bf16":
+        A = gemm_inputs.bf16_matrix(M, K, w.dist, sa_seed).cuda()
+        B = torch.zeros((N, K), dtype=torch.bfloat16, device="cuda")
+        d = min(N, K)
+        B[torch.arange(d), torch.arange(d)] = 1.0
+        C = _run(hk.HK_DTYPE_BF16, A, B, M, N, K, K, K, N)
+        want = A[:, :d]
+    else:
+        A8, sa = gemm_inputs.fp8_matrix(M, K, sa_seed)
+        A = A8.cuda()
+        B = torch.zeros((N, K), dtype=torch.uint8, device="cuda")
+        d = min(N, K)
+        B[torch.arange(d), torch.arange(d)] = 0x38  # e4m3 1.0
+        C = _run(hk.HK_DTYPE_FP8_E4M3, A, B, M, N, K, K, K, N, 2.0 ** -4, 8.0)
+        # 2^-4 * 8 = 0.5: every e4m3 value times 0.5 is an exact bf16 value
+        dec = oracle.e4m3_table()[gemm_inputs.bits(A8)[:, :d]] * 0.5
+        want = torch.from_numpy(oracle.bf16_round(dec).view(np.int16)).cuda()
+    ok = torch.equal(C[:, :d].view(torch.int16), want.view(torch.int16))
+    rest_zero = bool((C[:, d:].float() == 0).all()) if N > d else True
+    _say(name, "identity-like B", ok, rest_zero)
+    assert ok and rest_zero
+
+
+def test_k_tail_probe_ragged():
+    """Only the last 8 K positions of B are non-zero, so C is exactly the tail sum."""
+    w = gemm_inputs.WORKLOADS["bf16_mlp_ragged"]
+    M, N, K = w.M, w.N, w.K
+    A_cpu = gemm_inputs.bf16_matrix(M, K, "int4", 81)
+    B_cpu = torch.zeros((N, K), dtype=torch.bfloat16)
+    B_cpu[:, K - 8:] = gemm_inputs.bf16_matrix(N, 8, "int4", 82)
+    C = _run(hk.HK_DTYPE_BF16, A_cpu.cuda(), B_cpu.cuda(), M, N, K, K, K, N)
+    rng = np.random.default_rng(5)
+    rows, cols = _edge_samples(M, N, 256, rng, 4000)
+    got = _bits16(C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()])
+    ref, _ = oracle.gemm_sampled("bf16", gemm_inputs.bits(A_cpu).ravel(),
+                                 gemm_inputs.bits(B_cpu).ravel(), M, N, K, rows, cols)
+    st = oracle.compare(got, ref, exact=True)
+    assert st["ok"], st
+    assert np.count_nonzero(ref) > 0.5 * ref.size  # the probe really exercises the tail
