@@ -30,8 +30,8 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="bf16_8192")
     ap.add_argument("--schedule", default="auto")
     ap.add_argument("--grid-order", default="auto")
@@ -192,6 +192,7 @@ def main():
         fl = []
         for _ in range(max(5, a.steps // 5)):
             flush.fill_(1)
+            torch.cuda.synchronize()  # the flush must finish before the timed launch
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
                 s.record(stream)

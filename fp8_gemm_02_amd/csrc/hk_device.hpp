@@ -34,11 +34,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 constexpr uint32_t kOobOffset = 0x80000000u;
 
-// One 16-byte direct load from a buffer into LDS.  Lane i of the wave writes
-// its 16 bytes to lds_wave_base + 16*i; lds_wave_base must be wave-uniform.
-__device__ __forceinline__ void load_lds_b128(__amdgpu_buffer_rsrc_t rsrc,
-                                              HK_LDS void* lds_wave_base, uint32_t voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, lds_wave_base, 16, voffset, 0, 0, 0);
+// The same resource as four dwords, for the hand-issued direct loads below.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+// One 16-byte direct load from a buffer into LDS: lane i of the wave writes
+// its 16 bytes to lds_wave_base + 16*i (lds_wave_base is wave-uniform and goes
+// through M0), fetched from byte voffset + soffset of the buffer.  Issued as
+// inline assembly so that the compiler does not track the LDS write: the
+// kernels order these writes against their LDS reads with explicit
+// s_waitcnt vmcnt and workgroup barriers, and a compiler-inserted wait would
+// serialise the loads they deliberately keep in flight.
+__device__ __forceinline__ void load_lds_b128(i32x4 rsrc, HK_LDS void* lds_wave_base,
+                                              uint32_t voffset, uint32_t soffset) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soffset)
+        : "memory", "m0");
 }
 
 // ------------------------------------------------------------ MFMA wrappers
@@ -54,11 +72,14 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(i32x4 a, i32x4 b, f32x4 c) {
 
 // 16x16x128 with both operands in OCP E4M3 (format code 0) and unit block
 // scales (E8M0 exponent 127 = 2^0): each lane supplies 32 bytes of K.
-__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x4 a0, i32x4 a1, i32x4 b0, i32x4 b1,
-                                                    f32x4 c) {
-    const i32x8 a = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const i32x8 b = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Half c (0 = low 16 bytes, 1 = high 16 bytes) of a 32-byte fragment.
+__device__ __forceinline__ i32x4 half_of(i32x8 v, int c) {
+    return c == 0 ? __builtin_shufflevector(v, v, 0, 1, 2, 3)
+                  : __builtin_shufflevector(v, v, 4, 5, 6, 7);
 }
 
 // ------------------------------------------------------ schedule control
@@ -73,7 +94,12 @@ __device__ __forceinline__ void fenced_barrier() {
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4]
 // at 15:14, expcnt at 6:4, lgkmcnt at 11:8); a field at its maximum waits
 // for nothing.
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+template <int kVm>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(kVm >= 0 && kVm < 64, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0070); }
 

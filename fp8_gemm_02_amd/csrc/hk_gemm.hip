@@ -25,18 +25,20 @@
 
 extern "C" __global__ void __launch_bounds__(hk::kPP8Threads)
 hk_gemm_pp8_bf16(hk::GemmArgs g) {
-    __shared__ hk::i32x4 sA0[hk::kPP8StageI4], sB0[hk::kPP8StageI4];
-    __shared__ hk::i32x4 sA1[hk::kPP8StageI4], sB1[hk::kPP8StageI4];
-    hk::pp8_body<false, HK_SWZ>(g, (HK_LDS hk::i32x4*)sA0, (HK_LDS hk::i32x4*)sB0,
-                                (HK_LDS hk::i32x4*)sA1, (HK_LDS hk::i32x4*)sB1);
+    __shared__ hk::i32x4 alo0[hk::kPP8HalfI4], ahi0[hk::kPP8HalfI4], b0[hk::kPP8StageI4];
+    __shared__ hk::i32x4 alo1[hk::kPP8HalfI4], ahi1[hk::kPP8HalfI4], b1[hk::kPP8StageI4];
+    const hk::PP8Buf buf0 = {(HK_LDS hk::i32x4*)alo0, (HK_LDS hk::i32x4*)ahi0, (HK_LDS hk::i32x4*)b0};
+    const hk::PP8Buf buf1 = {(HK_LDS hk::i32x4*)alo1, (HK_LDS hk::i32x4*)ahi1, (HK_LDS hk::i32x4*)b1};
+    hk::pp8_body<false, HK_SWZ>(g, buf0, buf1);
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kPP8Threads)
 hk_gemm_pp8_fp8(hk::GemmArgs g) {
-    __shared__ hk::i32x4 sA0[hk::kPP8StageI4], sB0[hk::kPP8StageI4];
-    __shared__ hk::i32x4 sA1[hk::kPP8StageI4], sB1[hk::kPP8StageI4];
-    hk::pp8_body<true, HK_SWZ>(g, (HK_LDS hk::i32x4*)sA0, (HK_LDS hk::i32x4*)sB0,
-                               (HK_LDS hk::i32x4*)sA1, (HK_LDS hk::i32x4*)sB1);
+    __shared__ hk::i32x4 alo0[hk::kPP8HalfI4], ahi0[hk::kPP8HalfI4], b0[hk::kPP8StageI4];
+    __shared__ hk::i32x4 alo1[hk::kPP8HalfI4], ahi1[hk::kPP8HalfI4], b1[hk::kPP8StageI4];
+    const hk::PP8Buf buf0 = {(HK_LDS hk::i32x4*)alo0, (HK_LDS hk::i32x4*)ahi0, (HK_LDS hk::i32x4*)b0};
+    const hk::PP8Buf buf1 = {(HK_LDS hk::i32x4*)alo1, (HK_LDS hk::i32x4*)ahi1, (HK_LDS hk::i32x4*)b1};
+    hk::pp8_body<true, HK_SWZ>(g, buf0, buf1);
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kBasicThreads)

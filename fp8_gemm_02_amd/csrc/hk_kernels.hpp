@@ -64,15 +64,24 @@ __device__ __forceinline__ uint32_t swz_key(uint32_t row) {
 constexpr int kPP8Tile = 256;
 constexpr int kPP8Threads = 512;
 constexpr int kPP8StageI4 = kPP8Tile * kChunks;  // 16-byte chunks per operand per stage
+constexpr int kPP8HalfI4 = kPP8StageI4 / 2;       // one A region (128 rows)
+
+// LDS of one stage buffer: each region is its own array, so the compiler's
+// tracking of asynchronous LDS writes can tell a refill of one region from
+// reads of another.
+struct PP8Buf {
+    HK_LDS i32x4* alo;  // A tile rows 0-63 and 128-191 (16 KiB)
+    HK_LDS i32x4* ahi;  // A tile rows 64-127 and 192-255 (16 KiB)
+    HK_LDS i32x4* b;    // B tile rows 0-255 (32 KiB)
+};
 
 template <bool kFp8, int kSwz>
-__device__ __forceinline__ void pp8_body(const GemmArgs& g, HK_LDS i32x4* sA0, HK_LDS i32x4* sB0,
-                                         HK_LDS i32x4* sA1, HK_LDS i32x4* sB1) {
+__device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, const PP8Buf buf1) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Group 0 (waves 0-3) loads the A tile and owns output rows 0..127 of the
-    // tile; group 1 (waves 4-7) loads the B tile and owns rows 128..255.
-    // Within a group, wave wq owns the 64-column strip wq.
+    // Group 0 (waves 0-3) owns output rows 0..127 of the tile and issues all
+    // HBM->LDS loads; group 1 (waves 4-7) owns rows 128..255.  Within a group,
+    // wave wq owns the 64-column strip wq.
     const uint32_t grp = wave >> 2;
     const uint32_t wq = wave & 3u;
 
@@ -83,38 +92,72 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, HK_LDS i32x4* sA0, H
     const uint32_t kbytes = (uint32_t)g.K * (kFp8 ? 1u : 2u);
     const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
 
-    // ---- HBM -> LDS loads: this wave moves 8 blocks of 8 rows of its
-    // group's operand per stage; block b = 4i + wq holds tile rows 8b..8b+7
-    // and lane l lands on row 8b + l/8, physical chunk l%8.
-    const bool loads_a = (grp == 0);
-    const uint32_t ld_b = loads_a ? g.lda_b : g.ldb_b;
-    const int32_t rows_left = loads_a ? g.M - m0 : g.N - n0;
-    const uint8_t* src = loads_a ? g.A + (int64_t)m0 * ld_b : g.B + (int64_t)n0 * ld_b;
-    uint64_t span = (uint64_t)rows_left * ld_b;  // rows past the edge read as zero
-    if (span > kOobOffset) span = kOobOffset;
-    const auto rsrc = make_rsrc(src, (uint32_t)span);
-    const uint32_t lrow = wq * 8u + (lane >> 3);             // tile row for i = 0
-    const uint32_t lkc = (lane & 7u) ^ swz_key<kSwz>(lrow);  // logical chunk it must hold
-    const uint32_t voff0 = lrow * ld_b + lkc * 16u;
-    const uint32_t vstep = 32u * ld_b;                       // block b -> b + 4
-
-    auto issue_loads = [&](HK_LDS i32x4* dA, HK_LDS i32x4* dB, uint32_t t) {
-        HK_LDS i32x4* dst = loads_a ? dA : dB;
-        // K chunks past the end of the row (the K tail) read as zero
-        const bool kvalid = t * (uint32_t)kRowBytes + lkc * 16u < kbytes;
-        const uint32_t vo = voff0 + t * (uint32_t)kRowBytes;
+    // ---- HBM -> LDS.  A stage of an operand is 32 blocks of 8 rows; one
+    // 16-byte load per lane moves a block (lane l -> row 8b + l/8, physical
+    // chunk l%8, which holds logical chunk (l%8) ^ key(row)).  The regions of
+    // a stage buffer free up at different times: B and A-lo after the first
+    // memory phase of both groups, A-hi after the second.  Group 0 refills
+    // each region as soon as it is free:
+    //   batch HI(s): A-hi of stage s       (4 loads per wave), one stage ahead
+    //   batch LO(s): B and A-lo of stage s (12 loads per wave), two stages ahead
+    // so every batch has six phases to land.  Batches for stages past the end
+    // are issued anyway with every lane out of range (they only write zeros
+    // into regions nobody reads again), which keeps every wait count constant.
+    const uint32_t kc_lane = (lane & 7u) ^ swz_key<kSwz>(wq * 8u + (lane >> 3));
+    uint32_t span_a = 0, span_b = 0;
+    {
+        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;  // rows past the edge read as zero
+        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
+        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
+        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
+    }
+    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
+    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
+    const uint32_t vrow_a = (lane >> 3) * g.lda_b + kc_lane * 16u;
+    const uint32_t vrow_b = (lane >> 3) * g.ldb_b + kc_lane * 16u;
+    // This wave's blocks: region block r = wq + 4j.  In A-lo, region blocks
+    // 0-7 are tile blocks 0-7 and 8-15 are tile blocks 16-23; in A-hi, region
+    // blocks 0-7 are tile blocks 8-15 and 8-15 are tile blocks 24-31.
+    uint32_t vhi[4], vlo_a[4], vlo_b[8];
 #pragma unroll
-        for (uint32_t i = 0; i < 8; ++i)
-            load_lds_b128(rsrc, dst + (i * 4u + wq) * 64u, kvalid ? vo + i * vstep : kOobOffset);
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t rb = wq + 4u * j;
+        const uint32_t tile_lo = rb < 8 ? rb : rb + 8u;
+        vlo_a[j] = vrow_a + tile_lo * 8u * g.lda_b;
+        vhi[j] = vrow_a + (tile_lo + 8u) * 8u * g.lda_b;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vlo_b[j] = vrow_b + (wq + 4u * j) * 8u * g.ldb_b;
+
+    // One load of region block `block`; lanes whose chunk is at or past K (or
+    // any lane, for a stage past the end) read zero.
+    auto ld = [&](const i32x4& rs, HK_LDS i32x4* dst, uint32_t block, uint32_t voff,
+                  uint32_t s) {
+        // the stage offset rides in the (uniform) scalar offset; a masked lane's
+        // vector offset alone already lies past the end of the buffer
+        const uint32_t koff = s * (uint32_t)kRowBytes;
+        const bool ok = koff + kc_lane * 16u < kbytes;
+        load_lds_b128(rs, (HK_LDS void*)(dst + block * 64u), ok ? voff : kOobOffset, koff);
+    };
+    auto issue_hi = [&](const PP8Buf& d, uint32_t s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ld(rsrc_a, d.ahi, wq + 4u * j, vhi[j], s);
+    };
+    auto issue_lo = [&](const PP8Buf& d, uint32_t s) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ld(rsrc_b, d.b, wq + 4u * j, vlo_b[j], s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ld(rsrc_a, d.alo, wq + 4u * j, vlo_a[j], s);
     };
 
     // ---- LDS -> register fragments.  Fragment rows start at multiples of 16,
-    // so the swizzle key depends on the lane only.
+    // so the swizzle key depends on the lane only.  Group g's A rows are
+    // region rows g*64 .. g*64+63 of both A-lo and A-hi.
     const uint32_t r16 = lane & 15u;
     const uint32_t g4 = lane >> 4;
     const uint32_t key = swz_key<kSwz>(r16);
-    const uint32_t fa0 = (grp * 128u + r16) * kChunks + ((0u + g4) ^ key);
-    const uint32_t fa1 = (grp * 128u + r16) * kChunks + ((4u + g4) ^ key);
+    const uint32_t fa0 = (grp * 64u + r16) * kChunks + ((0u + g4) ^ key);
+    const uint32_t fa1 = (grp * 64u + r16) * kChunks + ((4u + g4) ^ key);
     const uint32_t fb0 = (wq * 64u + r16) * kChunks + ((0u + g4) ^ key);
     const uint32_t fb1 = (wq * 64u + r16) * kChunks + ((4u + g4) ^ key);
 
@@ -123,10 +166,15 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, HK_LDS i32x4* sA0, H
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    i32x4 af[4][2], bfr[4][2];
+    // A fragment is the lane's two 16-byte chunks of one row block: K chunks
+    // g and g+4 of the stage.  BF16 feeds them to two 16x16x32 MFMAs (one
+    // K slice each); FP8 feeds the pair to one 16x16x128 MFMA.
+    auto frag = [](const HK_LDS i32x4* p, uint32_t o0, uint32_t o1) {
+        return __builtin_shufflevector(p[o0], p[o1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 
     // matrix-core cluster over output row blocks mbase..mbase+3
-    auto mma = [&](const int mbase) {
+    auto mma = [&](const int mbase, const i32x8 (&af)[4], const i32x8 (&bfr)[4]) {
         if constexpr (!kFp8) {
 #pragma unroll
             for (int c = 0; c < 2; ++c)
@@ -134,72 +182,72 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, HK_LDS i32x4* sA0, H
                 for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < 4; ++nb)
-                        acc[mbase + mb][nb] =
-                            mfma_bf16_16x16x32(bfr[nb][c], af[mb][c], acc[mbase + mb][nb]);
+                        acc[mbase + mb][nb] = mfma_bf16_16x16x32(half_of(bfr[nb], c),
+                                                                 half_of(af[mb], c),
+                                                                 acc[mbase + mb][nb]);
         } else {
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb)
-                    acc[mbase + mb][nb] = mfma_fp8_16x16x128(bfr[nb][0], bfr[nb][1], af[mb][0],
-                                                             af[mb][1], acc[mbase + mb][nb]);
+                    acc[mbase + mb][nb] =
+                        mfma_fp8_16x16x128(bfr[nb], af[mb], acc[mbase + mb][nb]);
         }
     };
 
-    // One stage t, as four barrier-separated phases.  Group 0 runs
-    // M C M C, group 1 runs the same one phase later, so in every phase one
-    // group issues memory work while the other issues matrix-core work.
-    auto stage = [&](const HK_LDS i32x4* rA, const HK_LDS i32x4* rB, HK_LDS i32x4* wA,
-                     HK_LDS i32x4* wB, uint32_t t) {
-        // memory: A-side fragments of row blocks 0-3, all B-side fragments,
-        // and this group's half of stage t+1 into the other buffer (free:
-        // every wave finished reading stage t-1 before this phase began)
+    // One stage t as four barrier-separated phases.  Group 0 runs
+    // M1 C1 M2 C2, group 1 runs the same one phase later, so in every phase
+    // one group issues memory work while the other issues matrix-core work.
+    // cur holds stage t; oth holds stage t+1 (or is being filled with it).
+    const bool loader = (grp == 0);
+    auto stage = [&](const PP8Buf& cur, const PP8Buf& oth, uint32_t t) {
+        i32x8 af[4], bfr[4];
+        // M1: A-lo fragments (row blocks 0-3) and all B fragments of stage t;
+        // the loader sends HI(t+1) into the other buffer, whose A-hi was last
+        // read in the previous stage's second memory phase
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            af[mb][0] = rA[fa0 + mb * 128];
-            af[mb][1] = rA[fa1 + mb * 128];
-        }
+        for (int mb = 0; mb < 4; ++mb) af[mb] = frag(cur.alo, fa0 + mb * 128, fa1 + mb * 128);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            bfr[nb][0] = rB[fb0 + nb * 128];
-            bfr[nb][1] = rB[fb1 + nb * 128];
-        }
-        if (t + 1 < nk) issue_loads(wA, wB, t + 1);
+        for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag(cur.b, fb0 + nb * 128, fb1 + nb * 128);
+        if (loader) issue_hi(oth, t + 1);
         wait_lgkmcnt0();
         fenced_barrier();
-        // compute
+        // C1; then HI(t) must have landed (newer in flight: LO(t+1), HI(t+1))
         __builtin_amdgcn_s_setprio(1);
-        mma(0);
+        mma(0, af, bfr);
         __builtin_amdgcn_s_setprio(0);
+        if (loader) wait_vmcnt<16>();
         fenced_barrier();
-        // memory: A-side fragments of row blocks 4-7
+        // M2: A-hi fragments (row blocks 4-7); every wave has finished with
+        // this buffer's B and A-lo, so the loader sends LO(t+2) into them
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            af[mb][0] = rA[fa0 + (mb + 4) * 128];
-            af[mb][1] = rA[fa1 + (mb + 4) * 128];
-        }
-        if (grp == 1) wait_vmcnt0();  // group 1's loads of stage t+1 have landed
+        for (int mb = 0; mb < 4; ++mb) af[mb] = frag(cur.ahi, fa0 + mb * 128, fa1 + mb * 128);
+        if (loader) issue_lo(cur, t + 2);
         wait_lgkmcnt0();
         fenced_barrier();
-        // compute
+        // C2; then LO(t+1) must have landed (newer in flight: HI(t+1), LO(t+2))
         __builtin_amdgcn_s_setprio(1);
-        mma(4);
+        mma(4, af, bfr);
         __builtin_amdgcn_s_setprio(0);
-        if (grp == 0) wait_vmcnt0();  // group 0's loads of stage t+1 have landed
+        if (loader) wait_vmcnt<16>();
         fenced_barrier();
     };
 
-    if (nk > 0) {
-        issue_loads(sA0, sB0, 0);
-        wait_vmcnt0();
+    // prologue: LO(0), HI(0), LO(1) in flight; LO(0) must have landed
+    if (loader) {
+        issue_lo(buf0, 0);
+        issue_hi(buf0, 0);
+        issue_lo(buf1, 1);
+        wait_vmcnt<16>();
     }
     fenced_barrier();
     if (grp == 1) fenced_barrier();  // start group 1 one phase behind
     for (uint32_t t = 0; t < nk; t += 2) {
-        stage(sA0, sB0, sA1, sB1, t);
-        if (t + 1 < nk) stage(sA1, sB1, sA0, sB0, t + 1);
+        stage(buf0, buf1, t);
+        if (t + 1 < nk) stage(buf1, buf0, t + 1);
     }
     if (grp == 0) fenced_barrier();  // match group 1's barrier count
+    wait_vmcnt0();                   // no LDS write may outlive the workgroup
 
     // ---- epilogue: lane holds C[m][n..n+3] for each (mb, nb)
     const int32_t mrow = m0 + (int32_t)(grp * 128u + r16);
@@ -296,8 +344,10 @@ __device__ __forceinline__ void basic_body(const GemmArgs& g, HK_LDS i32x4* sA, 
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
                 if constexpr (kFp8) {
-                    acc[mb][nb] = mfma_fp8_16x16x128(bfr[nb][0], bfr[nb][1], af[mb][0], af[mb][1],
-                                                     acc[mb][nb]);
+                    acc[mb][nb] = mfma_fp8_16x16x128(
+                        __builtin_shufflevector(bfr[nb][0], bfr[nb][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                        __builtin_shufflevector(af[mb][0], af[mb][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                        acc[mb][nb]);
                 } else {
                     acc[mb][nb] = mfma_bf16_16x16x32(bfr[nb][0], af[mb][0], acc[mb][nb]);
                     acc[mb][nb] = mfma_bf16_16x16x32(bfr[nb][1], af[mb][1], acc[mb][nb]);

@@ -296,7 +296,9 @@ def test_full_size_identity_like_B(name):
         # 2^-4 * 8 = 0.5: every e4m3 value times 0.5 is an exact bf16 value
         dec = oracle.e4m3_table()[gemm_inputs.bits(A8)[:, :d]] * 0.5
         want = torch.from_numpy(oracle.bf16_round(dec).view(np.int16)).cuda()
-    ok = torch.equal(C[:, :d].view(torch.int16), want.view(torch.int16))
+    # +0 and -0 compare equal: an e4m3 -0 times 1 summed from +0 is +0
+    st = oracle.compare(_bits16(C[:, :d]), _bits16(want), exact=True)
+    ok = st["ok"]
     rest_zero = bool((C[:, d:].float() == 0).all()) if N > d else True
     _say(name, "identity-like B", ok, rest_zero)
     assert ok and rest_zero
