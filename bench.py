@@ -42,7 +42,23 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--extra", action="store_true",
                     help="also time each launch after an L2/LLC flush and report it")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="instead of the GEMM, run one plain device-to-device copy of BYTES "
+                         "bytes (torch copy_) 5 times; the HBM byte counters read on it "
+                         "calibrate those read on the GEMM")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int):
+    """A plain copy kernel of known size: reads nbytes, writes nbytes per launch."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
 def traffic_from_profiles(kernel: str, workload: str):
@@ -108,6 +124,9 @@ def main():
         print("bench.py measures one GPU only; --gpus %d is not supported (every box here has "
               "a single MI355X, and this GEMM has no multi-GPU path)" % a.gpus, file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
     import torch
     import gemm_inputs
     import fp8_gemm_02_amd as hk

@@ -11,6 +11,7 @@
 
 namespace hk {
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -49,7 +50,7 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t byte
 // serialise the loads they deliberately keep in flight.
 __device__ __forceinline__ void load_lds_b128(i32x4 rsrc, HK_LDS void* lds_wave_base,
                                               uint32_t voffset, uint32_t soffset) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)lds_wave_base;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -76,6 +77,22 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// 32x32x16 bf16: lane l supplies 8 bf16 of row l%32 of the 32 x 16 "A"
+// operand (K positions 8*(l/32) .. +7) and likewise of column l%32 of "B".
+// The result lane l holds column l%32, rows 8j + 4*(l/32) + v in element
+// 4j + v (j, v = 0..3).
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(i32x4 a, i32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 32x32x64 with both operands in OCP E4M3 (format code 0) and unit block
+// scales: lane l supplies 32 bytes of K of row (column) l%32; same result
+// layout as the bf16 32x32 form.
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // Half c (0 = low 16 bytes, 1 = high 16 bytes) of a 32-byte fragment.
 __device__ __forceinline__ i32x4 half_of(i32x8 v, int c) {
     return c == 0 ? __builtin_shufflevector(v, v, 0, 1, 2, 3)
@@ -84,11 +101,27 @@ __device__ __forceinline__ i32x4 half_of(i32x8 v, int c) {
 
 // ------------------------------------------------------ schedule control
 //
-// A workgroup barrier that the compiler may not move any instruction across.
+// A workgroup barrier that the compiler may not move any instruction across:
+// the empty asm statements stop IR passes from moving memory accesses over it,
+// sched_barrier stops the machine scheduler from moving anything.
 __device__ __forceinline__ void fenced_barrier() {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+// Make v look read and rewritten at this point, so that the instructions
+// computing it stay before it (matrix-core intrinsics have no side effects
+// and could otherwise be sunk past later barriers).
+__device__ __forceinline__ void pin(f32x4& v) { asm volatile("" : "+v"(v)); }
+template <int kM, int kN>
+__device__ __forceinline__ void pin_all(f32x4 (&acc)[kM][kN]) {
+#pragma unroll
+    for (int i = 0; i < kM; ++i)
+#pragma unroll
+        for (int j = 0; j < kN; ++j) pin(acc[i][j]);
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] at bits 3:0 and vmcnt[5:4]

@@ -13,10 +13,6 @@
 #include "hk_gemm.h"
 #include "hk_kernels.hpp"
 
-#ifndef HK_SWZ
-#define HK_SWZ 1
-#endif
-
 #define HK_VERSION 100  // 0.1.0
 
 // ------------------------------------------------------------------ kernels
@@ -29,7 +25,7 @@ hk_gemm_pp8_bf16(hk::GemmArgs g) {
     __shared__ hk::i32x4 alo1[hk::kPP8HalfI4], ahi1[hk::kPP8HalfI4], b1[hk::kPP8StageI4];
     const hk::PP8Buf buf0 = {(HK_LDS hk::i32x4*)alo0, (HK_LDS hk::i32x4*)ahi0, (HK_LDS hk::i32x4*)b0};
     const hk::PP8Buf buf1 = {(HK_LDS hk::i32x4*)alo1, (HK_LDS hk::i32x4*)ahi1, (HK_LDS hk::i32x4*)b1};
-    hk::pp8_body<false, HK_SWZ>(g, buf0, buf1);
+    hk::pp8_body<false, 1>(g, buf0, buf1);
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kPP8Threads)
@@ -38,7 +34,32 @@ hk_gemm_pp8_fp8(hk::GemmArgs g) {
     __shared__ hk::i32x4 alo1[hk::kPP8HalfI4], ahi1[hk::kPP8HalfI4], b1[hk::kPP8StageI4];
     const hk::PP8Buf buf0 = {(HK_LDS hk::i32x4*)alo0, (HK_LDS hk::i32x4*)ahi0, (HK_LDS hk::i32x4*)b0};
     const hk::PP8Buf buf1 = {(HK_LDS hk::i32x4*)alo1, (HK_LDS hk::i32x4*)ahi1, (HK_LDS hk::i32x4*)b1};
-    hk::pp8_body<true, HK_SWZ>(g, buf0, buf1);
+    hk::pp8_body<true, 1>(g, buf0, buf1);
+}
+
+// Two stage buffers of an A and a B image (32 KiB each): 128 KiB.
+#define HK_IL4_LDS                                                                   \
+    __shared__ hk::i32x4 a0[hk::kIL4StageI4], b0[hk::kIL4StageI4], a1[hk::kIL4StageI4], \
+        b1[hk::kIL4StageI4];                                                           \
+    const hk::IL4Buf buf0 = {(HK_LDS hk::i32x4*)a0, (HK_LDS hk::i32x4*)b0};            \
+    const hk::IL4Buf buf1 = {(HK_LDS hk::i32x4*)a1, (HK_LDS hk::i32x4*)b1}
+
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_bf16(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_body<false>(g, buf0, buf1);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_fp8(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_body<true>(g, buf0, buf1);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kI8Threads)
+hk_gemm_i8_bf16(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::i8_body(g, buf0, buf1);
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kBasicThreads)
@@ -106,7 +127,7 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
     if (dtype != HK_DTYPE_BF16 && dtype != HK_DTYPE_FP8_E4M3) return HK_ERROR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return HK_ERROR_INVALID_VALUE;
     if (opts) {
-        if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_BASIC)
+        if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_INTERLEAVE8)
             return HK_ERROR_INVALID_VALUE;
         if (opts->grid_order < HK_GRID_AUTO || opts->grid_order > HK_GRID_XCD)
             return HK_ERROR_INVALID_VALUE;
@@ -145,8 +166,10 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
                          lda % chunk == 0 && ldb % chunk == 0 &&
                          lda_b * hk::kPP8Tile < kMaxRowBytes && ldb_b * hk::kPP8Tile < kMaxRowBytes;
     if (sched == HK_SCHEDULE_AUTO) sched = fast_ok ? HK_SCHEDULE_PINGPONG8 : HK_SCHEDULE_BASIC;
-    if (sched == HK_SCHEDULE_INTERLEAVE4) return HK_ERROR_NOT_SUPPORTED;
-    if (sched == HK_SCHEDULE_PINGPONG8 && !fast_ok) return HK_ERROR_NOT_SUPPORTED;
+    if ((sched == HK_SCHEDULE_PINGPONG8 || sched == HK_SCHEDULE_INTERLEAVE4 ||
+         sched == HK_SCHEDULE_INTERLEAVE8) && !fast_ok)
+        return HK_ERROR_NOT_SUPPORTED;
+    if (sched == HK_SCHEDULE_INTERLEAVE8 && dtype != HK_DTYPE_BF16) return HK_ERROR_NOT_SUPPORTED;
 
     const bool fp8 = dtype == HK_DTYPE_FP8_E4M3;
     if (sched == HK_SCHEDULE_PINGPONG8) {
@@ -155,6 +178,18 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
         p->lds_bytes = 4 * hk::kPP8StageI4 * 16;
         p->kernel = fp8 ? (const void*)hk_gemm_pp8_fp8 : (const void*)hk_gemm_pp8_bf16;
         p->name = fp8 ? "hk_gemm_pp8_fp8" : "hk_gemm_pp8_bf16";
+    } else if (sched == HK_SCHEDULE_INTERLEAVE8) {
+        p->tile = hk::kIL4Tile;
+        p->threads = hk::kI8Threads;
+        p->lds_bytes = 4 * hk::kIL4StageI4 * 16;
+        p->kernel = (const void*)hk_gemm_i8_bf16;
+        p->name = "hk_gemm_i8_bf16";
+    } else if (sched == HK_SCHEDULE_INTERLEAVE4) {
+        p->tile = hk::kIL4Tile;
+        p->threads = hk::kIL4Threads;
+        p->lds_bytes = 4 * hk::kIL4StageI4 * 16;
+        p->kernel = fp8 ? (const void*)hk_gemm_il4_fp8 : (const void*)hk_gemm_il4_bf16;
+        p->name = fp8 ? "hk_gemm_il4_fp8" : "hk_gemm_il4_bf16";
     } else {
         p->tile = hk::kBasicTile;
         p->threads = hk::kBasicThreads;

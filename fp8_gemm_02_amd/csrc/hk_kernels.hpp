@@ -215,6 +215,7 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         // C1; then HI(t) must have landed (newer in flight: LO(t+1), HI(t+1))
         __builtin_amdgcn_s_setprio(1);
         mma(0, af, bfr);
+        pin_all(acc);
         __builtin_amdgcn_s_setprio(0);
         if (loader) wait_vmcnt<16>();
         fenced_barrier();
@@ -228,6 +229,7 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         // C2; then LO(t+1) must have landed (newer in flight: HI(t+1), LO(t+2))
         __builtin_amdgcn_s_setprio(1);
         mma(4, af, bfr);
+        pin_all(acc);
         __builtin_amdgcn_s_setprio(0);
         if (loader) wait_vmcnt<16>();
         fenced_barrier();
@@ -265,6 +267,403 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
                     if constexpr (kFp8) v *= g.scale;
                     store_bf16x4(crow + n, n, g.N, v, g.c_align);
                 }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------- 4-wave interleave
+//
+// "How to make AMD GPUs go brrr", section "Intra-processor scheduling: wave
+// patterns": one wave per SIMD, each interleaving its own HBM->LDS loads and
+// LDS reads with its matrix-core instructions.  A 256 x 256 tile of C per
+// workgroup of 4 waves in a 2 x 2 arrangement; each wave owns a 128 x 128
+// sub-tile as 4 x 4 blocks of 32 x 32 (256 fp32 accumulators per lane, which
+// the compiler keeps in the accumulation registers).  The 32 x 32 matrix-core
+// shapes are used because they run at the full rate on gfx950 for both
+// dtypes (v_mfma_f32_32x32x16_bf16, v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// LDS: two stage buffers, each an A and a B image of 256 rows x 128 bytes of
+// K (64 BF16 or 128 E4M3), the same swizzled row layout as the ping-pong
+// kernel.  A stage is processed as two halves (K bytes 0-63 and 64-127); the
+// fragments of one half (A and B, 8 x 32 bytes per lane) are read while the
+// matrix cores consume the other half's:
+//
+//   half 0 of stage t:  MFMA on F(t, 0)  |  read F(t, 1)
+//   -- wait for F(t, 1) and stage t+1's loads, workgroup barrier --
+//   half 1 of stage t:  MFMA on F(t, 1)  |  read F(t+1, 0), load stage t+2
+//
+// The barrier is the only one per stage: past it, every wave has finished
+// reading stage t (so its buffer may be refilled with stage t+2) and every
+// wave's share of stage t+1 has landed (so it may be read).
+constexpr int kIL4Tile = 256;
+constexpr int kIL4Threads = 256;
+constexpr int kIL4StageI4 = kIL4Tile * kChunks;  // 16-byte chunks per operand per stage
+
+struct IL4Buf {
+    HK_LDS i32x4* a;
+    HK_LDS i32x4* b;
+};
+
+// Swizzle of the 4-wave kernel's images: logical chunk c of row r sits at
+// physical chunk c ^ il4_key(r).  Its fragment reads put 32 consecutive lanes
+// on 32 consecutive rows at one chunk, and the LDS serves rows r and r+16 in
+// the same cycle: keying on r % 8 alone costs two conflict cycles per
+// ds_read_b128 (measured with SQ_LDS_BANK_CONFLICT), flipping bit 0 of the
+// key for rows 8-15 of every 16 removes them.
+__device__ __forceinline__ uint32_t il4_key(uint32_t row) {
+    return (row & 7u) ^ ((row >> 3) & 1u);
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void il4_body(const GemmArgs& g, const IL4Buf buf0, const IL4Buf buf1) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
+    const uint32_t wn = wave & 1u;  // B rows (C columns) wn*128 .. +127
+
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, g.grid, &tm, &tn);
+    const int32_t m0 = (int32_t)tm * kIL4Tile;
+    const int32_t n0 = (int32_t)tn * kIL4Tile;
+    const uint32_t kbytes = (uint32_t)g.K * (kFp8 ? 1u : 2u);
+    const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+
+    // ---- HBM -> LDS.  A stage of an operand is 32 blocks of 8 rows; block b
+    // is one 16-byte load per lane (lane l -> row 8b + l/8, physical chunk
+    // l%8, which holds logical chunk (l%8) ^ il4_key(row)).  Wave w sends
+    // blocks w + 4j (j = 0..7) of A and of B: 16 loads per stage.  Its blocks
+    // all have the parity of w, so the key is a per-lane constant.
+    const uint32_t kc_lane = (lane & 7u) ^ il4_key((wave & 1u) * 8u + (lane >> 3));
+    uint32_t span_a, span_b;
+    {
+        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;  // rows past the edge read as zero
+        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
+        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
+        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
+    }
+    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
+    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
+    uint32_t voff_a[8], voff_b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t row = (wave + 4u * j) * 8u + (lane >> 3);
+        voff_a[j] = row * g.lda_b + kc_lane * 16u;
+        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
+    }
+    // Load i (0-7: A block wave+4i, 8-15: B block wave+4(i-8)) of stage s into
+    // buffer d.  Lanes whose chunk lies at or past K (every lane, for a stage
+    // past the end) read zeros, which keeps every wait count constant.
+    auto send = [&](const IL4Buf& d, uint32_t s, int i) {
+        const uint32_t koff = s * (uint32_t)kRowBytes;
+        const bool ok = koff + kc_lane * 16u < kbytes;
+        const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
+        if (i < 8)
+            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), ok ? voff_a[i & 7] : kOobOffset,
+                          koff);
+        else
+            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), ok ? voff_b[i & 7] : kOobOffset,
+                          koff);
+    };
+
+    // ---- LDS -> fragments.  For half h of a stage, the lane holds two
+    // 16-byte chunks of row (block base + l%32): logical chunks 4h + l/32 and
+    // 4h + 2 + l/32.  Lanes 0-31 and 32-63 thus cover the half's four chunks,
+    // identically for A and B.  Block bases are multiples of 32, so the
+    // swizzle key depends on the lane only.
+    const uint32_t r32 = lane & 31u;
+    const uint32_t hi = lane >> 5;
+    const uint32_t key = il4_key(r32);
+    uint32_t fo[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        fo[h][0] = r32 * kChunks + ((4u * h + hi) ^ key);
+        fo[h][1] = r32 * kChunks + ((4u * h + 2u + hi) ^ key);
+    }
+    const uint32_t arow = wm * 128u;
+    const uint32_t brow = wn * 128u;
+    // fragment f of half h: f = 0..3 A blocks, 4..7 B blocks; read c = 0, 1
+    auto read = [&](const IL4Buf& d, int h, int f, int c) -> i32x4 {
+        const HK_LDS i32x4* base = f < 4 ? d.a + (arow + 32u * (uint32_t)f) * kChunks
+                                         : d.b + (brow + 32u * (uint32_t)(f - 4)) * kChunks;
+        return base[fo[h][c]];
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    // Matrix-core work of one half: MFMA number q of the half's list.
+    //  BF16: 32 MFMAs, K slice c = q / 16 outer, block (mb, nb) inner, so a
+    //        block's two slices are 16 instructions apart;
+    //  FP8:  16 MFMAs, one per block.
+    constexpr int kMfmaPerHalf = kFp8 ? 16 : 32;
+    auto mfma = [&](const i32x4 (&fr)[8][2], int q) {
+        const int blk = q & 15;
+        const int mb = blk >> 2, nb = blk & 3;
+        if constexpr (kFp8) {
+            acc[mb][nb] = mfma_fp8_32x32x64(
+                __builtin_shufflevector(fr[4 + nb][0], fr[4 + nb][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                __builtin_shufflevector(fr[mb][0], fr[mb][1], 0, 1, 2, 3, 4, 5, 6, 7),
+                acc[mb][nb]);
+        } else {
+            const int c = q >> 4;
+            acc[mb][nb] = mfma_bf16_32x32x16(fr[4 + nb][c], fr[mb][c], acc[mb][nb]);
+        }
+    };
+
+    i32x4 fx[8][2], fy[8][2];  // fragments of the two halves in flight
+    // With one wave per SIMD, a memory instruction delays the wave's next
+    // matrix-core instruction, so the memory work of a half is spread evenly
+    // over its MFMAs (bursts of it measured slower).  Fragments are read in the
+    // order the MFMA list consumes them (A block 0, B blocks 0-3, A blocks
+    // 1-3), so that the next half's first MFMAs wait for only the first
+    // reads; the compiler waits for each fragment just before its first use.
+    auto rd = [&](i32x4 (&fr)[8][2], const IL4Buf& d, int h, int r) {
+        constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+        // BF16 consumes slice 0 of every block before slice 1; FP8 needs both
+        // chunks of a block at once
+        const int f = kFp8 ? kOrder[r >> 1] : kOrder[r & 7];
+        const int c = kFp8 ? (r & 1) : (r >> 3);
+        fr[f][c] = read(d, h, f, c);
+    };
+    // memory slot of MFMA q: BF16 (32 per half) every other MFMA, FP8 (16
+    // per half, 64 cycles each) every MFMA
+    constexpr int kStep = kMfmaPerHalf / 16;
+    // Half 0 of stage t: MFMAs on fx; reads of half 1 into fy.
+    auto half0 = [&](const IL4Buf& cur) {
+#pragma unroll
+        for (int q = 0; q < kMfmaPerHalf; ++q) {
+            mfma(fx, q);
+            if (q % kStep == kStep - 1) rd(fy, cur, 1, q / kStep);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // Half 1 of stage t: MFMAs on fy; the loads of stage t+2 and the reads of
+    // stage t+1's half 0 into fx.
+    auto half1 = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+#pragma unroll
+        for (int q = 0; q < kMfmaPerHalf; ++q) {
+            mfma(fy, q);
+            if (q % kStep == kStep - 1) {
+                send(cur, t + 2, q / kStep);
+                rd(fx, nxt, 0, q / kStep);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto stage = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+        half0(cur);
+        wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
+        wait_vmcnt0();    // this wave's share of stage t+1 has landed
+        fenced_barrier();
+        half1(cur, nxt, t);
+    };
+
+    // prologue: stages 0 and 1 in flight, stage 0 landed, F(0, 0) read
+#pragma unroll
+    for (int i = 0; i < 16; ++i) send(buf0, 0, i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) send(buf1, 1, i);
+    wait_vmcnt<16>();
+    fenced_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rd(fx, buf0, 0, r);
+    // An even number of stages keeps the loop body free of branches; a stage
+    // past the end of K reads only zeros and adds exactly nothing.
+    for (uint32_t t = 0; t < nk; t += 2) {
+        stage(buf0, buf1, t);
+        stage(buf1, buf0, t + 1);
+    }
+    wait_all();  // no LDS write may outlive the workgroup
+
+    // ---- epilogue.  Block (mb, nb) of C^T: lane l holds C row
+    // m = arow + mb*32 + l%32 at columns n = brow + nb*32 + 8j + 4(l/32) + v,
+    // v = 0..3, in acc[mb][nb][4j + v].
+    const int32_t mbase = m0 + (int32_t)(arow + r32);
+    const int32_t nbase = n0 + (int32_t)(brow + hi * 4u);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int32_t m = mbase + mb * 32;
+        if (m < g.M) {
+            uint16_t* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int32_t n = nbase + nb * 32 + j * 8;
+                    if (n < g.N) {
+                        f32x4 v = {acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1],
+                                   acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
+                        if constexpr (kFp8) v *= g.scale;
+                        store_bf16x4(crow + n, n, g.N, v, g.c_align);
+                    }
+                }
+        }
+    }
+}
+
+// ------------------------------------------------------- 8-wave interleave
+//
+// Eight waves (two per SIMD), each interleaving its own memory work with its
+// own matrix-core instructions, so that both waves of a SIMD issue
+// v_mfma_f32_16x16x32_bf16 at the same time.  On gfx950 one wave cannot
+// issue that instruction back to back at the full rate, two waves can, and
+// it costs less energy per FLOP than the 32 x 32 shape, which is what sets
+// the sustained clock of a power-bound GEMM.  Wave w owns output rows
+// (w / 4) * 128 .. +127 and columns (w % 4) * 64 .. +63 of the 256 x 256 tile
+// as 8 x 4 blocks of 16 x 16 (128 accumulators per lane).
+//
+// LDS and pipeline as in the 4-wave kernel, with the two K slices of 32
+// (chunks 0-3 and 4-7 of a 128-byte stage row) in place of its halves:
+//
+//   slice 0 of stage t:  MFMA on F(t, 0)  |  read F(t, 1)
+//   -- wait for F(t, 1) and stage t+1's loads, workgroup barrier --
+//   slice 1 of stage t:  MFMA on F(t, 1)  |  load stage t+2, read F(t+1, 0)
+//
+// The image rows use the ping-pong kernel's key (row % 8), conflict-free for
+// 16-row fragment reads.  BF16 only.
+constexpr int kI8Threads = 512;
+
+__device__ __forceinline__ void i8_body(const GemmArgs& g, const IL4Buf buf0, const IL4Buf buf1) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wm = wave >> 2;  // A rows wm*128 .. +127
+    const uint32_t wn = wave & 3u;  // B rows (C columns) wn*64 .. +63
+
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, g.grid, &tm, &tn);
+    const int32_t m0 = (int32_t)tm * kIL4Tile;
+    const int32_t n0 = (int32_t)tn * kIL4Tile;
+    const uint32_t kbytes = (uint32_t)g.K * 2u;
+    const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+
+    // ---- HBM -> LDS: block b = 8 rows, lane l -> row 8b + l/8, physical
+    // chunk l%8 holding logical chunk (l%8) ^ (l/8).  Wave w sends blocks
+    // w + 8j (j = 0..3) of A and of B: 8 loads per stage.
+    const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
+    uint32_t span_a, span_b;
+    {
+        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;
+        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
+        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
+        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
+    }
+    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
+    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
+    uint32_t voff_a[4], voff_b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t row = (wave + 8u * j) * 8u + (lane >> 3);
+        voff_a[j] = row * g.lda_b + kc_lane * 16u;
+        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
+    }
+    // load i (0-3: A block wave+8i, 4-7: B block wave+8(i-4)) of stage s
+    auto send = [&](const IL4Buf& d, uint32_t s, int i) {
+        const uint32_t koff = s * (uint32_t)kRowBytes;
+        const bool ok = koff + kc_lane * 16u < kbytes;
+        const uint32_t blk = wave + 8u * (uint32_t)(i & 3);
+        if (i < 4)
+            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), ok ? voff_a[i & 3] : kOobOffset,
+                          koff);
+        else
+            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), ok ? voff_b[i & 3] : kOobOffset,
+                          koff);
+    };
+
+    // ---- LDS -> fragments.  Slice s of a 16-row block: lane l holds 8 bf16
+    // of row (block base + l%16), logical chunk 4s + l/16.
+    const uint32_t r16 = lane & 15u;
+    const uint32_t g4 = lane >> 4;
+    const uint32_t fo0 = r16 * kChunks + ((0u + g4) ^ (r16 & 7u));
+    const uint32_t fo1 = r16 * kChunks + ((4u + g4) ^ (r16 & 7u));
+    const uint32_t arow = wm * 128u;
+    const uint32_t brow = wn * 64u;
+    // fragment f of slice s: f = 0..7 A blocks, 8..11 B blocks
+    auto read = [&](const IL4Buf& d, int s, int f) -> i32x4 {
+        const HK_LDS i32x4* base = f < 8 ? d.a + (arow + 16u * (uint32_t)f) * kChunks
+                                         : d.b + (brow + 16u * (uint32_t)(f - 8)) * kChunks;
+        return base[s == 0 ? fo0 : fo1];
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // MFMA q of a slice: B block nb = q % 4 as the "A" operand, A block
+    // mb = q / 4 as the "B" operand (C^T, so a lane holds 4 consecutive
+    // columns of one C row).  Fragments are read in the order the list
+    // consumes them: A block 0, B blocks 0-3, A blocks 1-7.
+    i32x4 fx[12], fy[12];
+    auto mfma = [&](const i32x4 (&fr)[12], int q) {
+        const int mb = q >> 2, nb = q & 3;
+        acc[mb][nb] = mfma_bf16_16x16x32(fr[8 + nb], fr[mb], acc[mb][nb]);
+    };
+    auto rd = [&](i32x4 (&fr)[12], const IL4Buf& d, int s, int r) {
+        constexpr int kOrder[12] = {0, 8, 9, 10, 11, 1, 2, 3, 4, 5, 6, 7};
+        fr[kOrder[r]] = read(d, s, kOrder[r]);
+    };
+    auto slice0 = [&](const IL4Buf& cur) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            mfma(fx, q);
+            if ((q & 1) && q < 24) rd(fy, cur, 1, q >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto slice1 = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            mfma(fy, q);
+            if (q < 16) {
+                if (q & 1) rd(fx, nxt, 0, q >> 1);
+                else send(cur, t + 2, q >> 1);
+            } else if ((q & 1) && q < 24) {
+                rd(fx, nxt, 0, 8 + ((q - 16) >> 1));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto stage = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+        slice0(cur);
+        wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
+        wait_vmcnt0();    // this wave's share of stage t+1 has landed
+        fenced_barrier();
+        slice1(cur, nxt, t);
+    };
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) send(buf0, 0, i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) send(buf1, 1, i);
+    wait_vmcnt<8>();
+    fenced_barrier();
+#pragma unroll
+    for (int r = 0; r < 12; ++r) rd(fx, buf0, 0, r);
+    for (uint32_t t = 0; t < nk; t += 2) {
+        stage(buf0, buf1, t);
+        stage(buf1, buf0, t + 1);
+    }
+    wait_all();
+
+    // ---- epilogue: lane holds C[m][n..n+3] for each (mb, nb)
+    const int32_t mrow = m0 + (int32_t)(arow + r16);
+    const int32_t ncol = n0 + (int32_t)(brow + g4 * 4u);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int32_t m = mrow + mb * 16;
+        if (m < g.M) {
+            uint16_t* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int32_t n = ncol + nb * 16;
+                if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb], g.c_align);
             }
         }
     }

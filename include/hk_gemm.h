@@ -76,7 +76,8 @@ typedef enum hk_schedule {
     HK_SCHEDULE_AUTO = 0,
     HK_SCHEDULE_PINGPONG8 = 1,
     HK_SCHEDULE_INTERLEAVE4 = 2,
-    HK_SCHEDULE_BASIC = 3
+    HK_SCHEDULE_BASIC = 3,
+    HK_SCHEDULE_INTERLEAVE8 = 4
 } hk_schedule;
 
 /*

@@ -178,3 +178,20 @@ def test_plan_rejects_huge_strides():
     with pytest.raises(hk.HKError) as e:
         _plan(hk.HK_DTYPE_BF16, 8, 8, 8, lda=2 ** 30, ldb=8)
     assert e.value.status == hk.HK_ERROR_NOT_SUPPORTED
+
+
+@pytest.mark.parametrize("schedule,dtype,name,threads", [
+    ("interleave4", hk.HK_DTYPE_BF16, "hk_gemm_il4_bf16", 256),
+    ("interleave4", hk.HK_DTYPE_FP8_E4M3, "hk_gemm_il4_fp8", 256),
+    ("interleave8", hk.HK_DTYPE_BF16, "hk_gemm_i8_bf16", 512),
+    ("pingpong8", hk.HK_DTYPE_FP8_E4M3, "hk_gemm_pp8_fp8", 512)])
+def test_plan_explicit_schedules(schedule, dtype, name, threads):
+    p = _plan(dtype, 8192, 8192, 8192, schedule=schedule)
+    assert p["kernel_name"] == name and p["threads"] == threads
+    assert (p["tile_m"], p["tile_n"]) == (256, 256) and p["lds_bytes"] == 131072
+
+
+def test_interleave8_is_bf16_only():
+    with pytest.raises(hk.HKError) as e:
+        _plan(hk.HK_DTYPE_FP8_E4M3, 256, 256, 256, schedule="interleave8")
+    assert e.value.status == hk.HK_ERROR_NOT_SUPPORTED

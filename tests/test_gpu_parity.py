@@ -110,7 +110,7 @@ def test_fp8_ragged_full(M, N, K, integer):
     _full_check("fp8", A, B, M, N, K, K, K, exact=integer, sa=sa, sb=sb)
 
 
-@pytest.mark.parametrize("schedule", ["pingpong8", "basic"])
+@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "basic"])
 @pytest.mark.parametrize("grid_order", ["row_major", "xcd"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_every_variant(schedule, grid_order, dtype):
@@ -122,6 +122,22 @@ def test_every_variant(schedule, grid_order, dtype):
         B, sb = gemm_inputs.fp8_matrix(N, K, 14)
     _full_check(dtype, A, B, M, N, K, K, K, exact=False, sa=sa, sb=sb, schedule=schedule,
                 grid_order=grid_order)
+
+
+@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "interleave8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(513, 769, 1040), (256, 256, 128), (300, 40, 16)])
+def test_fast_schedules_ragged_integer(schedule, dtype, M, N, K):
+    """Bit-exact on integer-valued inputs: edge tiles, K tails and odd stage counts."""
+    if schedule == "interleave8" and dtype == "fp8":
+        pytest.skip("the 8-wave interleave kernel is BF16 only")
+    if dtype == "bf16":
+        A, B, sa, sb = _bf16(M, K, "int4", M + 3), _bf16(N, K, "int4", N + 4), 1.0, 1.0
+    else:
+        A, _ = gemm_inputs.fp8_matrix(M, K, M + 5, integer=True)
+        B, _ = gemm_inputs.fp8_matrix(N, K, N + 6, integer=True)
+        sa, sb = 0.5, 4.0
+    _full_check(dtype, A, B, M, N, K, K, K, exact=True, sa=sa, sb=sb, schedule=schedule)
 
 
 @pytest.mark.parametrize("group_m,window", [(1, 256), (3, 100), (16, 64), (8, 7)])
