@@ -50,7 +50,7 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t byte
 // serialise the loads they deliberately keep in flight.
 __device__ __forceinline__ void load_lds_b128(i32x4 rsrc, HK_LDS void* lds_wave_base,
                                               uint32_t voffset, uint32_t soffset) {
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_wave_base);
+    const uint32_t m0v = (uint32_t)(uintptr_t)lds_wave_base;
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
@@ -91,6 +91,25 @@ __device__ __forceinline__ f32x16 mfma_bf16_32x32x16(i32x4 a, i32x4 b, f32x16 c)
 // layout as the bf16 32x32 form.
 __device__ __forceinline__ f32x16 mfma_fp8_32x32x64(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// The same instruction with the accumulator pinned to the accumulation
+// registers (AGPRs): for kernels that keep 256 accumulators per lane, the
+// compiler otherwise splits them between register files and copies them back
+// and forth inside the loop.  Issued as inline assembly, so the compiler
+// inserts no wait states for it: callers leave room between writing acc with
+// ordinary instructions and this, and between this and reading acc
+// (acc_settle below).  The compiler still waits for the loads that produce
+// a and b, which are ordinary register operands.
+__device__ __forceinline__ void mfma_bf16_16x16x32_pinned(f32x4& acc, i32x4 a, i32x4 b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states that cover a matrix-core result (or an accumulator written by
+// ordinary instructions) before its next reader: 4 x 8 idle cycles, more
+// than the longest dependency the instructions above need.
+__device__ __forceinline__ void acc_settle() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 // Half c (0 = low 16 bytes, 1 = high 16 bytes) of a 32-byte fragment.

@@ -47,7 +47,11 @@ hk_gemm_pp8_fp8(hk::GemmArgs g) {
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
 hk_gemm_il4_bf16(hk::GemmArgs g) {
     HK_IL4_LDS;
+#ifdef HK_IL4_BF16_32
     hk::il4_body<false>(g, buf0, buf1);
+#else
+    hk::il4_bf16_body(g, buf0, buf1);
+#endif
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
@@ -165,7 +169,11 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     const bool fast_ok = aligned(A, 16) && aligned(B, 16) && K % chunk == 0 &&
                          lda % chunk == 0 && ldb % chunk == 0 &&
                          lda_b * hk::kPP8Tile < kMaxRowBytes && ldb_b * hk::kPP8Tile < kMaxRowBytes;
-    if (sched == HK_SCHEDULE_AUTO) sched = fast_ok ? HK_SCHEDULE_PINGPONG8 : HK_SCHEDULE_BASIC;
+    // Measured on MI355X at 8192^3: the 4-wave interleave is the faster BF16
+    // kernel, the 8-wave ping-pong the faster FP8 one.
+    if (sched == HK_SCHEDULE_AUTO)
+        sched = !fast_ok ? HK_SCHEDULE_BASIC
+                         : (dtype == HK_DTYPE_BF16 ? HK_SCHEDULE_INTERLEAVE4 : HK_SCHEDULE_PINGPONG8);
     if ((sched == HK_SCHEDULE_PINGPONG8 || sched == HK_SCHEDULE_INTERLEAVE4 ||
          sched == HK_SCHEDULE_INTERLEAVE8) && !fast_ok)
         return HK_ERROR_NOT_SUPPORTED;

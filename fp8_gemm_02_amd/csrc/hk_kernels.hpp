@@ -25,6 +25,8 @@
 // consecutive columns of one C row, which it stores as one 8-byte write.
 #pragma once
 
+#include <type_traits>
+
 #include "hk_device.hpp"
 #include "hk_grid.hpp"
 
@@ -129,25 +131,27 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
 #pragma unroll
     for (int j = 0; j < 8; ++j) vlo_b[j] = vrow_b + (wq + 4u * j) * 8u * g.ldb_b;
 
-    // One load of region block `block`; lanes whose chunk is at or past K (or
-    // any lane, for a stage past the end) read zero.
-    auto ld = [&](const i32x4& rs, HK_LDS i32x4* dst, uint32_t block, uint32_t voff,
-                  uint32_t s) {
+    // One load of region block `block`.  Masked: lanes whose chunk is at or
+    // past K (or any lane, for a stage past the end) read zero; the main loop,
+    // whose stages all lie inside K, skips that select.
+    auto ld = [&](auto masked, const i32x4& rs, HK_LDS i32x4* dst, uint32_t block,
+                  uint32_t voff, uint32_t s) {
         // the stage offset rides in the (uniform) scalar offset; a masked lane's
         // vector offset alone already lies past the end of the buffer
         const uint32_t koff = s * (uint32_t)kRowBytes;
-        const bool ok = koff + kc_lane * 16u < kbytes;
-        load_lds_b128(rs, (HK_LDS void*)(dst + block * 64u), ok ? voff : kOobOffset, koff);
+        if constexpr (decltype(masked)::value)
+            voff = koff + kc_lane * 16u < kbytes ? voff : kOobOffset;
+        load_lds_b128(rs, (HK_LDS void*)(dst + block * 64u), voff, koff);
     };
-    auto issue_hi = [&](const PP8Buf& d, uint32_t s) {
+    auto issue_hi = [&](auto masked, const PP8Buf& d, uint32_t s) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ld(rsrc_a, d.ahi, wq + 4u * j, vhi[j], s);
+        for (int j = 0; j < 4; ++j) ld(masked, rsrc_a, d.ahi, wq + 4u * j, vhi[j], s);
     };
-    auto issue_lo = [&](const PP8Buf& d, uint32_t s) {
+    auto issue_lo = [&](auto masked, const PP8Buf& d, uint32_t s) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ld(rsrc_b, d.b, wq + 4u * j, vlo_b[j], s);
+        for (int j = 0; j < 8; ++j) ld(masked, rsrc_b, d.b, wq + 4u * j, vlo_b[j], s);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ld(rsrc_a, d.alo, wq + 4u * j, vlo_a[j], s);
+        for (int j = 0; j < 4; ++j) ld(masked, rsrc_a, d.alo, wq + 4u * j, vlo_a[j], s);
     };
 
     // ---- LDS -> register fragments.  Fragment rows start at multiples of 16,
@@ -200,7 +204,7 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
     // one group issues memory work while the other issues matrix-core work.
     // cur holds stage t; oth holds stage t+1 (or is being filled with it).
     const bool loader = (grp == 0);
-    auto stage = [&](const PP8Buf& cur, const PP8Buf& oth, uint32_t t) {
+    auto stage = [&](auto masked, const PP8Buf& cur, const PP8Buf& oth, uint32_t t) {
         i32x8 af[4], bfr[4];
         // M1: A-lo fragments (row blocks 0-3) and all B fragments of stage t;
         // the loader sends HI(t+1) into the other buffer, whose A-hi was last
@@ -209,7 +213,7 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         for (int mb = 0; mb < 4; ++mb) af[mb] = frag(cur.alo, fa0 + mb * 128, fa1 + mb * 128);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag(cur.b, fb0 + nb * 128, fb1 + nb * 128);
-        if (loader) issue_hi(oth, t + 1);
+        if (loader) issue_hi(masked, oth, t + 1);
         wait_lgkmcnt0();
         fenced_barrier();
         // C1; then HI(t) must have landed (newer in flight: LO(t+1), HI(t+1))
@@ -223,7 +227,7 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         // this buffer's B and A-lo, so the loader sends LO(t+2) into them
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) af[mb] = frag(cur.ahi, fa0 + mb * 128, fa1 + mb * 128);
-        if (loader) issue_lo(cur, t + 2);
+        if (loader) issue_lo(masked, cur, t + 2);
         wait_lgkmcnt0();
         fenced_barrier();
         // C2; then LO(t+1) must have landed (newer in flight: HI(t+1), LO(t+2))
@@ -236,17 +240,27 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
     };
 
     // prologue: LO(0), HI(0), LO(1) in flight; LO(0) must have landed
+    const std::true_type masked;
+    const std::false_type unmasked;
     if (loader) {
-        issue_lo(buf0, 0);
-        issue_hi(buf0, 0);
-        issue_lo(buf1, 1);
+        issue_lo(masked, buf0, 0);
+        issue_hi(masked, buf0, 0);
+        issue_lo(masked, buf1, 1);
         wait_vmcnt<16>();
     }
     fenced_barrier();
     if (grp == 1) fenced_barrier();  // start group 1 one phase behind
-    for (uint32_t t = 0; t < nk; t += 2) {
-        stage(buf0, buf1, t);
-        if (t + 1 < nk) stage(buf1, buf0, t + 1);
+    // Stage pair (t, t+1) loads up to stage t+3, all inside K while
+    // t + 4 <= the number of whole stages.
+    const uint32_t nk_whole = kbytes / kRowBytes;
+    uint32_t t = 0;
+    for (; t + 4 <= nk_whole; t += 2) {
+        stage(unmasked, buf0, buf1, t);
+        stage(unmasked, buf1, buf0, t + 1);
+    }
+    for (; t < nk; t += 2) {
+        stage(masked, buf0, buf1, t);
+        if (t + 1 < nk) stage(masked, buf1, buf0, t + 1);
     }
     if (grp == 0) fenced_barrier();  // match group 1's barrier count
     wait_vmcnt0();                   // no LDS write may outlive the workgroup
@@ -354,16 +368,15 @@ __device__ __forceinline__ void il4_body(const GemmArgs& g, const IL4Buf buf0, c
     // Load i (0-7: A block wave+4i, 8-15: B block wave+4(i-8)) of stage s into
     // buffer d.  Lanes whose chunk lies at or past K (every lane, for a stage
     // past the end) read zeros, which keeps every wait count constant.
-    auto send = [&](const IL4Buf& d, uint32_t s, int i) {
+    auto send = [&](auto masked, const IL4Buf& d, uint32_t s, int i) {
         const uint32_t koff = s * (uint32_t)kRowBytes;
-        const bool ok = koff + kc_lane * 16u < kbytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
+        uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
+        if constexpr (decltype(masked)::value) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
         if (i < 8)
-            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), ok ? voff_a[i & 7] : kOobOffset,
-                          koff);
+            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
         else
-            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), ok ? voff_b[i & 7] : kOobOffset,
-                          koff);
+            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
     };
 
     // ---- LDS -> fragments.  For half h of a stage, the lane holds two
@@ -445,39 +458,49 @@ __device__ __forceinline__ void il4_body(const GemmArgs& g, const IL4Buf buf0, c
     };
     // Half 1 of stage t: MFMAs on fy; the loads of stage t+2 and the reads of
     // stage t+1's half 0 into fx.
-    auto half1 = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+    auto half1 = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
 #pragma unroll
         for (int q = 0; q < kMfmaPerHalf; ++q) {
             mfma(fy, q);
             if (q % kStep == kStep - 1) {
-                send(cur, t + 2, q / kStep);
+                send(masked, cur, t + 2, q / kStep);
                 rd(fx, nxt, 0, q / kStep);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto stage = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+    auto stage = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
         half0(cur);
         wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
         wait_vmcnt0();    // this wave's share of stage t+1 has landed
         fenced_barrier();
-        half1(cur, nxt, t);
+        half1(masked, cur, nxt, t);
     };
 
     // prologue: stages 0 and 1 in flight, stage 0 landed, F(0, 0) read
+    const std::true_type masked;
+    const std::false_type unmasked;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(buf0, 0, i);
+    for (int i = 0; i < 16; ++i) send(masked, buf0, 0, i);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(buf1, 1, i);
+    for (int i = 0; i < 16; ++i) send(masked, buf1, 1, i);
     wait_vmcnt<16>();
     fenced_barrier();
 #pragma unroll
     for (int r = 0; r < 16; ++r) rd(fx, buf0, 0, r);
     // An even number of stages keeps the loop body free of branches; a stage
     // past the end of K reads only zeros and adds exactly nothing.
-    for (uint32_t t = 0; t < nk; t += 2) {
-        stage(buf0, buf1, t);
-        stage(buf1, buf0, t + 1);
+    // Stage pair (t, t+1) loads stages t+2 and t+3, all inside K while
+    // t + 4 <= the number of whole stages.
+    const uint32_t nk_whole = kbytes / kRowBytes;
+    uint32_t t = 0;
+    for (; t + 4 <= nk_whole; t += 2) {
+        stage(unmasked, buf0, buf1, t);
+        stage(unmasked, buf1, buf0, t + 1);
+    }
+    for (; t < nk; t += 2) {
+        stage(masked, buf0, buf1, t);
+        stage(masked, buf1, buf0, t + 1);
     }
     wait_all();  // no LDS write may outlive the workgroup
 
@@ -503,6 +526,168 @@ __device__ __forceinline__ void il4_body(const GemmArgs& g, const IL4Buf buf0, c
                         store_bf16x4(crow + n, n, g.N, v, g.c_align);
                     }
                 }
+        }
+    }
+}
+
+// BF16 form of the 4-wave interleave: v_mfma_f32_16x16x32_bf16, which on
+// gfx950 costs about 12% less energy per FLOP than the 32 x 32 shape when the
+// matrix cores are kept busy (the sustained clock of this power-bound GEMM
+// follows the energy per stage).  Each wave's 128 x 128 sub-tile is 8 x 8
+// blocks of 16 x 16 (256 accumulators per lane); a stage's two K slices of 32
+// (chunks 0-3 and 4-7) take the place of the halves above.  Fragment reads
+// put 16 lanes on 16 rows at one chunk, for which the key row % 8 is
+// conflict-free.
+__device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf buf0,
+                                              const IL4Buf buf1) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
+    const uint32_t wn = wave & 1u;  // B rows (C columns) wn*128 .. +127
+
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, g.grid, &tm, &tn);
+    const int32_t m0 = (int32_t)tm * kIL4Tile;
+    const int32_t n0 = (int32_t)tn * kIL4Tile;
+    const uint32_t kbytes = (uint32_t)g.K * 2u;
+    const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+
+    // ---- HBM -> LDS: block b = 8 rows, lane l -> row 8b + l/8, physical
+    // chunk l%8 holding logical chunk (l%8) ^ (l/8).  Wave w sends blocks
+    // w + 4j (j = 0..7) of A and of B: 16 loads per stage.
+    const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
+    uint32_t span_a, span_b;
+    {
+        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;
+        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
+        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
+        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
+    }
+    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
+    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
+    uint32_t voff_a[8], voff_b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t row = (wave + 4u * j) * 8u + (lane >> 3);
+        voff_a[j] = row * g.lda_b + kc_lane * 16u;
+        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
+    }
+    // Load i (0-7: A block wave+4i, 8-15: B block wave+4(i-8)) of stage s
+    // into buffer d.  kMasked: lanes whose chunk lies at or past K (every
+    // lane, for a stage past the end) read zeros; the main loop, whose stages
+    // all lie inside K, skips that select.
+    auto send = [&](auto masked, const IL4Buf& d, uint32_t s, int i) {
+        constexpr bool kMasked = decltype(masked)::value;
+        const uint32_t koff = s * (uint32_t)kRowBytes;
+        const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
+        uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
+        if constexpr (kMasked) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
+        if (i < 8)
+            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
+        else
+            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
+    };
+
+    // ---- LDS -> fragments.  Slice s of a 16-row block: lane l holds 8 bf16
+    // of row (block base + l%16), logical chunk 4s + l/16.
+    const uint32_t r16 = lane & 15u;
+    const uint32_t g4 = lane >> 4;
+    const uint32_t fo0 = r16 * kChunks + ((0u + g4) ^ (r16 & 7u));
+    const uint32_t fo1 = r16 * kChunks + ((4u + g4) ^ (r16 & 7u));
+    const uint32_t arow = wm * 128u;
+    const uint32_t brow = wn * 128u;
+    // fragment f of slice s: f = 0..7 A blocks, 8..15 B blocks
+    auto read = [&](const IL4Buf& d, int s, int f) -> i32x4 {
+        const HK_LDS i32x4* base = f < 8 ? d.a + (arow + 16u * (uint32_t)f) * kChunks
+                                         : d.b + (brow + 16u * (uint32_t)(f - 8)) * kChunks;
+        return base[s == 0 ? fo0 : fo1];
+    };
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc_settle();  // the zeroed accumulators before the first MFMA reads them
+
+    // MFMA q of a slice: B block q % 8 as the "A" operand, A block q / 8 as
+    // the "B" operand (C^T, so a lane holds 4 consecutive columns of a C row).
+    // Fragments are read in the order the list consumes them: A block 0,
+    // B blocks 0-7, A blocks 1-7.
+    i32x4 fx[16], fy[16];
+    auto mfma = [&](const i32x4 (&fr)[16], int q) {
+        const int mb = q >> 3, nb = q & 7;
+        mfma_bf16_16x16x32_pinned(acc[mb][nb], fr[8 + nb], fr[mb]);
+    };
+    auto rd = [&](i32x4 (&fr)[16], const IL4Buf& d, int s, int r) {
+        constexpr int kOrder[16] = {0, 8, 9, 10, 11, 12, 13, 14, 15, 1, 2, 3, 4, 5, 6, 7};
+        fr[kOrder[r]] = read(d, s, kOrder[r]);
+    };
+    // 64 MFMAs per slice; a memory instruction after every other one at most
+    auto slice0 = [&](const IL4Buf& cur) {
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            mfma(fx, q);
+            if ((q & 3) == 3) rd(fy, cur, 1, q >> 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto slice1 = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            mfma(fy, q);
+            if ((q & 3) == 1) send(masked, cur, t + 2, q >> 2);
+            if ((q & 3) == 3) rd(fx, nxt, 0, q >> 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto stage = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+        slice0(cur);
+        wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
+        wait_vmcnt0();    // this wave's share of stage t+1 has landed
+        fenced_barrier();
+        slice1(masked, cur, nxt, t);
+    };
+
+    const std::true_type masked;
+    const std::false_type unmasked;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) send(masked, buf0, 0, i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) send(masked, buf1, 1, i);
+    wait_vmcnt<16>();
+    fenced_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rd(fx, buf0, 0, r);
+    // Stages go in pairs (an even number of them: a stage past the end of K
+    // adds exactly nothing).  Pair (t, t+1) loads stages t+2 and t+3, which
+    // lie wholly inside K while t + 4 <= the number of whole stages.
+    const uint32_t nk_whole = kbytes / kRowBytes;
+    uint32_t t = 0;
+    for (; t + 4 <= nk_whole; t += 2) {
+        stage(unmasked, buf0, buf1, t);
+        stage(unmasked, buf1, buf0, t + 1);
+    }
+    for (; t < nk; t += 2) {
+        stage(masked, buf0, buf1, t);
+        stage(masked, buf1, buf0, t + 1);
+    }
+    wait_all();
+    acc_settle();  // the last MFMA results before the epilogue reads them
+
+    // ---- epilogue: lane holds C[m][n..n+3] for each (mb, nb)
+    const int32_t mrow = m0 + (int32_t)(arow + r16);
+    const int32_t ncol = n0 + (int32_t)(brow + g4 * 4u);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int32_t m = mrow + mb * 16;
+        if (m < g.M) {
+            uint16_t* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const int32_t n = ncol + nb * 16;
+                if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb], g.c_align);
+            }
         }
     }
 }
@@ -563,16 +748,15 @@ __device__ __forceinline__ void i8_body(const GemmArgs& g, const IL4Buf buf0, co
         voff_b[j] = row * g.ldb_b + kc_lane * 16u;
     }
     // load i (0-3: A block wave+8i, 4-7: B block wave+8(i-4)) of stage s
-    auto send = [&](const IL4Buf& d, uint32_t s, int i) {
+    auto send = [&](auto masked, const IL4Buf& d, uint32_t s, int i) {
         const uint32_t koff = s * (uint32_t)kRowBytes;
-        const bool ok = koff + kc_lane * 16u < kbytes;
         const uint32_t blk = wave + 8u * (uint32_t)(i & 3);
+        uint32_t vo = i < 4 ? voff_a[i & 3] : voff_b[i & 3];
+        if constexpr (decltype(masked)::value) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
         if (i < 4)
-            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), ok ? voff_a[i & 3] : kOobOffset,
-                          koff);
+            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
         else
-            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), ok ? voff_b[i & 3] : kOobOffset,
-                          koff);
+            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
     };
 
     // ---- LDS -> fragments.  Slice s of a 16-row block: lane l holds 8 bf16
@@ -617,38 +801,46 @@ __device__ __forceinline__ void i8_body(const GemmArgs& g, const IL4Buf buf0, co
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto slice1 = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+    auto slice1 = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
             mfma(fy, q);
             if (q < 16) {
                 if (q & 1) rd(fx, nxt, 0, q >> 1);
-                else send(cur, t + 2, q >> 1);
+                else send(masked, cur, t + 2, q >> 1);
             } else if ((q & 1) && q < 24) {
                 rd(fx, nxt, 0, 8 + ((q - 16) >> 1));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto stage = [&](const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+    auto stage = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
         slice0(cur);
         wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
         wait_vmcnt0();    // this wave's share of stage t+1 has landed
         fenced_barrier();
-        slice1(cur, nxt, t);
+        slice1(masked, cur, nxt, t);
     };
 
+    const std::true_type masked;
+    const std::false_type unmasked;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) send(buf0, 0, i);
+    for (int i = 0; i < 8; ++i) send(masked, buf0, 0, i);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) send(buf1, 1, i);
+    for (int i = 0; i < 8; ++i) send(masked, buf1, 1, i);
     wait_vmcnt<8>();
     fenced_barrier();
 #pragma unroll
     for (int r = 0; r < 12; ++r) rd(fx, buf0, 0, r);
-    for (uint32_t t = 0; t < nk; t += 2) {
-        stage(buf0, buf1, t);
-        stage(buf1, buf0, t + 1);
+    const uint32_t nk_whole = kbytes / kRowBytes;
+    uint32_t t = 0;
+    for (; t + 4 <= nk_whole; t += 2) {
+        stage(unmasked, buf0, buf1, t);
+        stage(unmasked, buf1, buf0, t + 1);
+    }
+    for (; t < nk; t += 2) {
+        stage(masked, buf0, buf1, t);
+        stage(masked, buf1, buf0, t + 1);
     }
     wait_all();
 

@@ -138,11 +138,11 @@ def _plan(dtype, M, N, K, lda=None, ldb=None, ldc=None, A=FAKE, B=FAKE, C=FAKE, 
                                          (8191, 28670, 8200, (32, 112))])
 def test_plan_fast_path_for_every_workload(M, N, K, tiles):
     p = _plan(hk.HK_DTYPE_BF16, M, N, K)
-    assert p["schedule"] == hk.HK_SCHEDULE_PINGPONG8
-    assert p["kernel_name"] == "hk_gemm_pp8_bf16"
+    assert p["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
+    assert p["kernel_name"] == "hk_gemm_il4_bf16"
     assert (p["tiles_m"], p["tiles_n"]) == tiles
     assert p["workgroups"] == tiles[0] * tiles[1]
-    assert p["threads"] == 512 and p["lds_bytes"] == 131072
+    assert p["threads"] == 256 and p["lds_bytes"] == 131072
     assert p["tile_k"] == 64
     assert p["grid_order"] == hk.HK_GRID_XCD
 
