@@ -118,6 +118,7 @@ struct Plan {
     int32_t threads;
     int32_t lds_bytes;
     int64_t tiles_m, tiles_n;
+    int64_t grid;  // workgroups launched (persistent kernels: at most one per CU)
     hk::GemmArgs args;
     const void* kernel;
     const char* name;
@@ -213,6 +214,9 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     if (p->tiles_m * p->tiles_n > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
 
     const int32_t cus = current_cu_count();
+    p->grid = p->tiles_m * p->tiles_n;
+    // the BF16 4-wave kernel is persistent: one workgroup per compute unit
+    if (sched == HK_SCHEDULE_INTERLEAVE4 && !fp8 && p->grid > cus) p->grid = cus;
     hk::GemmArgs& g = p->args;
     g.A = (const uint8_t*)A;
     g.B = (const uint8_t*)B;
@@ -241,7 +245,7 @@ __global__ void hk_zero_c(uint16_t* C, int64_t M, int64_t N, int64_t ldc) {
 }
 
 hk_status launch(const Plan& p, hipStream_t stream) {
-    const int64_t grid = p.tiles_m * p.tiles_n;
+    const int64_t grid = p.grid;
     hk::GemmArgs args = p.args;
     void* kargs[] = {&args};
     hipError_t e = hipLaunchKernel(p.kernel, dim3((uint32_t)grid), dim3((uint32_t)p.threads),
@@ -321,7 +325,7 @@ hk_status hk_gemm_plan(int32_t dtype, const void* A, const void* B, const void* 
     out->threads = p.threads;
     out->tiles_m = p.tiles_m;
     out->tiles_n = p.tiles_n;
-    out->workgroups = p.tiles_m * p.tiles_n;
+    out->workgroups = p.grid;
     out->lds_bytes = p.lds_bytes;
     out->group_m = p.args.grid.group_m;
     out->window = p.args.grid.window;

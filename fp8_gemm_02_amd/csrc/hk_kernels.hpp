@@ -534,37 +534,33 @@ __device__ __forceinline__ void il4_body(const GemmArgs& g, const IL4Buf buf0, c
 // gfx950 costs about 12% less energy per FLOP than the 32 x 32 shape when the
 // matrix cores are kept busy (the sustained clock of this power-bound GEMM
 // follows the energy per stage).  Each wave's 128 x 128 sub-tile is 8 x 8
-// blocks of 16 x 16 (256 accumulators per lane); a stage's two K slices of 32
-// (chunks 0-3 and 4-7) take the place of the halves above.  Fragment reads
-// put 16 lanes on 16 rows at one chunk, for which the key row % 8 is
-// conflict-free.
+// blocks of 16 x 16 (256 accumulators per lane, pinned to the accumulation
+// registers); a stage's two K slices of 32 (chunks 0-3 and 4-7) take the
+// place of the halves above.  Fragment reads put 16 lanes on 16 rows at one
+// chunk, for which the key row % 8 is conflict-free.
+//
+// Persistent: the grid has one workgroup per compute unit and workgroup b
+// computes tiles w = b, b + G, b + 2G, ... (G = grid size), which keeps the
+// workgroup-to-chiplet dealing and the co-resident windows of the tile map.
+// The stage pipeline runs through tile boundaries: the two stages loaded
+// past a tile's last one are the next tile's first two, so between tiles
+// only the store of C remains.
 __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf buf0,
                                               const IL4Buf buf1) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
     const uint32_t wn = wave & 1u;  // B rows (C columns) wn*128 .. +127
-
-    uint32_t tm, tn;
-    tile_of(blockIdx.x, g.grid, &tm, &tn);
-    const int32_t m0 = (int32_t)tm * kIL4Tile;
-    const int32_t n0 = (int32_t)tn * kIL4Tile;
+    const uint32_t total = (uint32_t)g.grid.tiles_m * (uint32_t)g.grid.tiles_n;
     const uint32_t kbytes = (uint32_t)g.K * 2u;
     const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+    const uint32_t nk_pad = (nk + 1u) & ~1u;  // stages run in pairs
+    const uint32_t nk_whole = kbytes / kRowBytes;
 
     // ---- HBM -> LDS: block b = 8 rows, lane l -> row 8b + l/8, physical
     // chunk l%8 holding logical chunk (l%8) ^ (l/8).  Wave w sends blocks
     // w + 4j (j = 0..7) of A and of B: 16 loads per stage.
     const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
-    uint32_t span_a, span_b;
-    {
-        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;
-        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
-        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
-        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
-    }
-    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
-    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
     uint32_t voff_a[8], voff_b[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -572,20 +568,40 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         voff_a[j] = row * g.lda_b + kc_lane * 16u;
         voff_b[j] = row * g.ldb_b + kc_lane * 16u;
     }
-    // Load i (0-7: A block wave+4i, 8-15: B block wave+4(i-8)) of stage s
-    // into buffer d.  kMasked: lanes whose chunk lies at or past K (every
-    // lane, for a stage past the end) read zeros; the main loop, whose stages
-    // all lie inside K, skips that select.
-    auto send = [&](auto masked, const IL4Buf& d, uint32_t s, int i) {
-        constexpr bool kMasked = decltype(masked)::value;
+    // Buffer resources of tile w's A and B row panels; rows past the matrix
+    // edge read as zero.  A tile past the end (w >= total) gets empty
+    // resources, so its loads read zeros and only keep the wait counts even.
+    struct Tile {
+        i32x4 ra, rb;
+        int32_t m0, n0;
+    };
+    auto tile = [&](uint32_t w) {
+        Tile t;
+        uint32_t tm = 0, tn = 0;
+        if (w < total) tile_of(w, g.grid, &tm, &tn);
+        t.m0 = (int32_t)tm * kIL4Tile;
+        t.n0 = (int32_t)tn * kIL4Tile;
+        const uint64_t sa = w < total ? (uint64_t)(g.M - t.m0) * g.lda_b : 0;
+        const uint64_t sb = w < total ? (uint64_t)(g.N - t.n0) * g.ldb_b : 0;
+        t.ra = make_rsrc_words(g.A + (int64_t)t.m0 * g.lda_b,
+                               (uint32_t)(sa > kOobOffset ? kOobOffset : sa));
+        t.rb = make_rsrc_words(g.B + (int64_t)t.n0 * g.ldb_b,
+                               (uint32_t)(sb > kOobOffset ? kOobOffset : sb));
+        return t;
+    };
+    // Load i (0-7: A block wave+4i, 8-15: B block wave+4(i-8)) of stage s of
+    // tile tt into buffer d.  Masked: lanes whose chunk lies at or past K
+    // (every lane, for a stage past the end) read zeros; the main loop, whose
+    // stages all lie inside K, skips that select.
+    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s, int i) {
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
         uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
-        if constexpr (kMasked) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
+        if constexpr (decltype(masked)::value) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
         if (i < 8)
-            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
+            load_lds_b128(tt.ra, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
         else
-            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
+            load_lds_b128(tt.rb, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
     };
 
     // ---- LDS -> fragments.  Slice s of a 16-row block: lane l holds 8 bf16
@@ -604,11 +620,13 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     };
 
     f32x4 acc[8][8];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_settle();  // the zeroed accumulators before the first MFMA reads them
+            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_settle();  // the zeroed accumulators before the first MFMA reads them
+    };
 
     // MFMA q of a slice: B block q % 8 as the "A" operand, A block q / 8 as
     // the "B" operand (C^T, so a lane holds 4 consecutive columns of a C row).
@@ -632,64 +650,93 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto slice1 = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+    // slice 1 of a stage: MFMAs on fy, the 16 loads of stage s of tile tt
+    // into cur, and the reads of the next stage's slice 0 from nxt into fx
+    auto slice1 = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
+                      const IL4Buf& nxt) {
 #pragma unroll
         for (int q = 0; q < 64; ++q) {
             mfma(fy, q);
-            if ((q & 3) == 1) send(masked, cur, t + 2, q >> 2);
+            if ((q & 3) == 1) send(masked, tt, cur, s, q >> 2);
             if ((q & 3) == 3) rd(fx, nxt, 0, q >> 2);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto stage = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
+    // stage t (in cur; the next stage in nxt) loading stage s of tile tt
+    auto stage = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
+                     const IL4Buf& nxt) {
         slice0(cur);
         wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
         wait_vmcnt0();    // this wave's share of stage t+1 has landed
         fenced_barrier();
-        slice1(masked, cur, nxt, t);
+        slice1(masked, tt, s, cur, nxt);
     };
 
     const std::true_type masked;
     const std::false_type unmasked;
+    uint32_t w = blockIdx.x;
+    Tile cur = tile(w);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, buf0, 0, i);
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf0, 0, i);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, buf1, 1, i);
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf1, 1, i);
     wait_vmcnt<16>();
     fenced_barrier();
 #pragma unroll
     for (int r = 0; r < 16; ++r) rd(fx, buf0, 0, r);
-    // Stages go in pairs (an even number of them: a stage past the end of K
-    // adds exactly nothing).  Pair (t, t+1) loads stages t+2 and t+3, which
-    // lie wholly inside K while t + 4 <= the number of whole stages.
-    const uint32_t nk_whole = kbytes / kRowBytes;
-    uint32_t t = 0;
-    for (; t + 4 <= nk_whole; t += 2) {
-        stage(unmasked, buf0, buf1, t);
-        stage(unmasked, buf1, buf0, t + 1);
-    }
-    for (; t < nk; t += 2) {
-        stage(masked, buf0, buf1, t);
-        stage(masked, buf1, buf0, t + 1);
-    }
-    wait_all();
-    acc_settle();  // the last MFMA results before the epilogue reads them
+    zero_acc();
 
-    // ---- epilogue: lane holds C[m][n..n+3] for each (mb, nb)
-    const int32_t mrow = m0 + (int32_t)(arow + r16);
-    const int32_t ncol = n0 + (int32_t)(brow + g4 * 4u);
+    for (;;) {
+        const uint32_t w_next = w + gridDim.x;
+        const Tile nxt = tile(w_next);
+        // Stage pair (t, t+1) loads stages t+2 and t+3, all inside K while
+        // t + 4 <= the number of whole stages.
+        uint32_t t = 0;
+        for (; t + 4 <= nk_whole; t += 2) {
+            stage(unmasked, cur, t + 2, buf0, buf1);
+            stage(unmasked, cur, t + 3, buf1, buf0);
+        }
+        // the last pairs: stages at or past the end of this tile's K load
+        // the next tile's first two stages (stage s of this tile is stage
+        // s - nk_pad of the next)
+        auto pick = [&](uint32_t s, uint32_t* s_out) {
+            const bool mine = s < nk_pad;
+            *s_out = mine ? s : s - nk_pad;
+            Tile r;
+            r.ra = mine ? cur.ra : nxt.ra;
+            r.rb = mine ? cur.rb : nxt.rb;
+            return r;
+        };
+        for (; t < nk_pad; t += 2) {
+            uint32_t s0, s1;
+            const Tile t0 = pick(t + 2, &s0);
+            stage(masked, t0, s0, buf0, buf1);
+            const Tile t1 = pick(t + 3, &s1);
+            stage(masked, t1, s1, buf1, buf0);
+        }
+        acc_settle();  // the last MFMA results before the epilogue reads them
+
+        // ---- epilogue: lane holds C[m][n..n+3] for each (mb, nb)
+        const int32_t mrow = cur.m0 + (int32_t)(arow + r16);
+        const int32_t ncol = cur.n0 + (int32_t)(brow + g4 * 4u);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-        const int32_t m = mrow + mb * 16;
-        if (m < g.M) {
-            uint16_t* crow = g.C + (int64_t)m * g.ldc;
+        for (int mb = 0; mb < 8; ++mb) {
+            const int32_t m = mrow + mb * 16;
+            if (m < g.M) {
+                uint16_t* crow = g.C + (int64_t)m * g.ldc;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
-                const int32_t n = ncol + nb * 16;
-                if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb], g.c_align);
+                for (int nb = 0; nb < 8; ++nb) {
+                    const int32_t n = ncol + nb * 16;
+                    if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb], g.c_align);
+                }
             }
         }
+        if (w_next >= total) break;
+        w = w_next;
+        cur = nxt;
+        zero_acc();
     }
+    wait_all();  // no LDS write may outlive the workgroup
 }
 
 // ------------------------------------------------------- 8-wave interleave

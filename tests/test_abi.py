@@ -141,7 +141,9 @@ def test_plan_fast_path_for_every_workload(M, N, K, tiles):
     assert p["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
     assert p["kernel_name"] == "hk_gemm_il4_bf16"
     assert (p["tiles_m"], p["tiles_n"]) == tiles
-    assert p["workgroups"] == tiles[0] * tiles[1]
+    # persistent: one workgroup per compute unit (256 on MI355X; the same
+    # count is assumed when no device is visible)
+    assert p["workgroups"] == min(tiles[0] * tiles[1], 256)
     assert p["threads"] == 256 and p["lds_bytes"] == 131072
     assert p["tile_k"] == 64
     assert p["grid_order"] == hk.HK_GRID_XCD
@@ -150,6 +152,7 @@ def test_plan_fast_path_for_every_workload(M, N, K, tiles):
 def test_plan_fp8():
     p = _plan(hk.HK_DTYPE_FP8_E4M3, 8192, 8192, 8192)
     assert p["kernel_name"] == "hk_gemm_pp8_fp8" and p["tile_k"] == 128
+    assert p["workgroups"] == 1024  # one workgroup per tile
 
 
 @pytest.mark.parametrize("K,lda,Aoff", [(60, 60, 0), (64, 66, 0), (64, 64, 2)])
