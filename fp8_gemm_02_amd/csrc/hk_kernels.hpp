@@ -641,12 +641,14 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         constexpr int kOrder[16] = {0, 8, 9, 10, 11, 12, 13, 14, 15, 1, 2, 3, 4, 5, 6, 7};
         fr[kOrder[r]] = read(d, s, kOrder[r]);
     };
-    // 64 MFMAs per slice; a memory instruction after every other one at most
+    // 64 MFMAs per slice.  Slice 0 reads the 16 fragments of slice 1 within
+    // its first 48 MFMAs, so that they have landed by the workgroup barrier
+    // that ends it.
     auto slice0 = [&](const IL4Buf& cur) {
 #pragma unroll
         for (int q = 0; q < 64; ++q) {
             mfma(fx, q);
-            if ((q & 3) == 3) rd(fy, cur, 1, q >> 2);
+            if (q % 3 == 2 && q / 3 < 16) rd(fy, cur, 1, q / 3);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
