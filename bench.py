@@ -176,7 +176,9 @@ def main():
     achieved = flops / (mean_ms * 1e-3) / 1e12
 
     out = {
-        "metric": "GEMM TFLOP/s at BF16 8192^3 and % of 2.5 PF BF16 peak (1 MI355X)",
+        "metric": ("GEMM TFLOP/s at BF16 8192^3 and % of 2.5 PF BF16 peak (1 MI355X)"
+                   if w.name == "bf16_8192" else
+                   "GEMM TFLOP/s, %s %dx%dx%d (1 MI355X)" % (w.dtype.upper(), w.M, w.N, w.K)),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -198,12 +200,23 @@ def main():
                       "min": round(durs_ms[0], 4), "max": round(durs_ms[-1], 4)},
     }
     tr = traffic_from_profiles(plan["kernel_name"], w.name)
-    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
-                       "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                       "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4),
-                       "traffic": tr[1] if tr else None,
-                       "algorithmic_flops_per_launch": flops,
-                       "algorithmic_bytes_per_launch": w.algorithmic_bytes}
+    # The binding roofline follows the arithmetic intensity: below the ridge
+    # (peak FLOP/s / peak HBM bytes/s) the shape is bound by HBM and the
+    # achieved rate is algorithmic bytes per launch over the launch time.
+    ai = flops / w.algorithmic_bytes
+    ridge = PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2),
+                           "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                           "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
+    else:
+        gbs = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    out["roofline"].update({"traffic": tr[1] if tr else None,
+                            "arithmetic_intensity": round(ai, 1), "ridge": round(ridge, 1),
+                            "algorithmic_flops_per_launch": flops,
+                            "algorithmic_bytes_per_launch": w.algorithmic_bytes})
 
     if a.extra:
         # per-launch time after flushing L2 and the last-level cache
