@@ -105,6 +105,15 @@ __device__ __forceinline__ void mfma_bf16_16x16x32_pinned(f32x4& acc, i32x4 a, i
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// 16x16x128 E4M3 with unit block scales (`one` holds E8M0 127), accumulator
+// pinned to the AGPRs like the BF16 form above.
+__device__ __forceinline__ void mfma_fp8_16x16x128_pinned(f32x4& acc, i32x8 a, i32x8 b,
+                                                          uint32_t one) {
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b), "v"(one));
+}
+
 // Wait states that cover a matrix-core result (or an accumulator written by
 // ordinary instructions) before its next reader: 4 x 8 idle cycles, more
 // than the longest dependency the instructions above need.

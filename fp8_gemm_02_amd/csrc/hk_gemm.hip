@@ -47,17 +47,13 @@ hk_gemm_pp8_fp8(hk::GemmArgs g) {
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
 hk_gemm_il4_bf16(hk::GemmArgs g) {
     HK_IL4_LDS;
-#ifdef HK_IL4_BF16_32
-    hk::il4_body<false>(g, buf0, buf1);
-#else
     hk::il4_bf16_body(g, buf0, buf1);
-#endif
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
 hk_gemm_il4_fp8(hk::GemmArgs g) {
     HK_IL4_LDS;
-    hk::il4_body<true>(g, buf0, buf1);
+    hk::il4_fp8_body(g, buf0, buf1);
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kI8Threads)
@@ -170,11 +166,9 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     const bool fast_ok = aligned(A, 16) && aligned(B, 16) && K % chunk == 0 &&
                          lda % chunk == 0 && ldb % chunk == 0 &&
                          lda_b * hk::kPP8Tile < kMaxRowBytes && ldb_b * hk::kPP8Tile < kMaxRowBytes;
-    // Measured on MI355X at 8192^3: the 4-wave interleave is the faster BF16
-    // kernel, the 8-wave ping-pong the faster FP8 one.
-    if (sched == HK_SCHEDULE_AUTO)
-        sched = !fast_ok ? HK_SCHEDULE_BASIC
-                         : (dtype == HK_DTYPE_BF16 ? HK_SCHEDULE_INTERLEAVE4 : HK_SCHEDULE_PINGPONG8);
+    // Measured on MI355X at 8192^3: the 4-wave interleave is the faster
+    // kernel for both dtypes.
+    if (sched == HK_SCHEDULE_AUTO) sched = fast_ok ? HK_SCHEDULE_INTERLEAVE4 : HK_SCHEDULE_BASIC;
     if ((sched == HK_SCHEDULE_PINGPONG8 || sched == HK_SCHEDULE_INTERLEAVE4 ||
          sched == HK_SCHEDULE_INTERLEAVE8) && !fast_ok)
         return HK_ERROR_NOT_SUPPORTED;
@@ -215,8 +209,8 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
 
     const int32_t cus = current_cu_count();
     p->grid = p->tiles_m * p->tiles_n;
-    // the BF16 4-wave kernel is persistent: one workgroup per compute unit
-    if (sched == HK_SCHEDULE_INTERLEAVE4 && !fp8 && p->grid > cus) p->grid = cus;
+    // the 4-wave kernels are persistent: one workgroup per compute unit
+    if (sched == HK_SCHEDULE_INTERLEAVE4 && p->grid > cus) p->grid = cus;
     hk::GemmArgs& g = p->args;
     g.A = (const uint8_t*)A;
     g.B = (const uint8_t*)B;

@@ -1,26 +1,29 @@
 // hk_kernels.hpp -- kernel bodies for C = A * B^T on gfx950.
 //
-// Two bodies share one data layout:
+// The fast bodies share one data layout.  A workgroup computes a 256 x 256
+// tile of C; K advances 128 bytes per stage (64 bf16 or 128 e4m3), so both
+// dtypes use the same LDS image: 256 rows x 8 chunks of 16 bytes per operand
+// per stage, two stages (128 KiB).  Operands go HBM -> LDS with direct buffer
+// loads (no register round trip), whose per-lane global addresses are
+// permuted so that the fixed lane -> LDS placement of those loads produces an
+// XOR-swizzled image that the fragment reads see without bank conflicts
+// ("How to make AMD GPUs go brrr", section "HipKittens memory-access
+// patterns": asynchronous HBM->shared loads, HBM address swizzling, one
+// swizzle per register layout).  Schedules ("Intra-processor scheduling:
+// wave patterns"):
 //
-//  * pp8_body: the fast path.  A 256 x 256 output tile per workgroup of 512
-//    threads (8 waves).  K advances 128 bytes per stage (64 bf16 or 128 e4m3),
-//    so both dtypes use the same LDS image: 256 rows x 8 chunks of 16 bytes per
-//    operand per stage, two stages (128 KiB).  Operands go HBM -> LDS with
-//    direct buffer loads (no register round trip), whose per-lane global
-//    addresses are permuted so that the fixed lane -> LDS placement of those
-//    loads produces an XOR-swizzled image that the fragment reads see without
-//    bank conflicts ("How to make AMD GPUs go brrr", section "HipKittens
-//    memory-access patterns": asynchronous HBM->shared loads, HBM address
-//    swizzling, one swizzle per register layout).  The waves form two groups
-//    of four (one wave per SIMD each) running the 8-wave ping-pong from the
-//    section "Intra-processor scheduling: wave patterns": while one group
-//    issues its cluster of matrix-core instructions, the other issues its
-//    cluster of LDS reads and HBM->LDS loads; workgroup barriers swap them.
-//
+//  * il4_bf16_body, il4_fp8_body: 4 waves (one per SIMD), each interleaving
+//    its own loads and LDS reads with its matrix-core instructions; one
+//    workgroup per compute unit walks its share of the tiles.  The default.
+//  * pp8_body: the 8-wave ping-pong; two groups of four waves swap between a
+//    cluster of matrix-core instructions and a cluster of memory work at
+//    workgroup barriers.
+//  * i8_body: 8 waves (two per SIMD), each interleaving like the 4-wave
+//    kernel (BF16 only).
 //  * basic_body: a plain fallback with no alignment requirements: 64 x 64
 //    tile, 4 waves, element-wise bounds-checked loads into LDS, one stage.
 //
-// Both compute C^T blocks on the matrix cores (B rows as the MFMA "A" operand,
+// All compute C^T blocks on the matrix cores (B rows as the MFMA "A" operand,
 // A rows as its "B" operand) so that each lane ends up holding four
 // consecutive columns of one C row, which it stores as one 8-byte write.
 #pragma once
@@ -61,7 +64,7 @@ __device__ __forceinline__ uint32_t swz_key(uint32_t row) {
     else return (row >> 1) & 7u;
 }
 
-// -------------------------------------------------------------- fast path
+// ----------------------------------------------------------- 8-wave ping-pong
 
 constexpr int kPP8Tile = 256;
 constexpr int kPP8Threads = 512;
@@ -292,20 +295,18 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
 // patterns": one wave per SIMD, each interleaving its own HBM->LDS loads and
 // LDS reads with its matrix-core instructions.  A 256 x 256 tile of C per
 // workgroup of 4 waves in a 2 x 2 arrangement; each wave owns a 128 x 128
-// sub-tile as 4 x 4 blocks of 32 x 32 (256 fp32 accumulators per lane, which
-// the compiler keeps in the accumulation registers).  The 32 x 32 matrix-core
-// shapes are used because they run at the full rate on gfx950 for both
-// dtypes (v_mfma_f32_32x32x16_bf16, v_mfma_scale_f32_32x32x64_f8f6f4).
+// sub-tile as 8 x 8 blocks of 16 x 16 (256 fp32 accumulators per lane,
+// pinned to the accumulation registers).
 //
 // LDS: two stage buffers, each an A and a B image of 256 rows x 128 bytes of
-// K (64 BF16 or 128 E4M3), the same swizzled row layout as the ping-pong
-// kernel.  A stage is processed as two halves (K bytes 0-63 and 64-127); the
-// fragments of one half (A and B, 8 x 32 bytes per lane) are read while the
-// matrix cores consume the other half's:
+// K (64 BF16 or 128 E4M3) with the row layout of the ping-pong kernel (key
+// row % 8, conflict-free for 16-row fragment reads).  A stage is split into
+// two slices of matrix-core work, and each wave reads the fragments of the
+// next slice while the matrix cores consume the current one's:
 //
-//   half 0 of stage t:  MFMA on F(t, 0)  |  read F(t, 1)
-//   -- wait for F(t, 1) and stage t+1's loads, workgroup barrier --
-//   half 1 of stage t:  MFMA on F(t, 1)  |  read F(t+1, 0), load stage t+2
+//   slice 0 of stage t:  MFMA  |  fragment reads
+//   -- wait for this wave's reads and stage t+1's loads; workgroup barrier --
+//   slice 1 of stage t:  MFMA  |  load stage t+2, read stage t+1's first fragments
 //
 // The barrier is the only one per stage: past it, every wave has finished
 // reading stage t (so its buffer may be refilled with stage t+2) and every
@@ -319,225 +320,14 @@ struct IL4Buf {
     HK_LDS i32x4* b;
 };
 
-// Swizzle of the 4-wave kernel's images: logical chunk c of row r sits at
-// physical chunk c ^ il4_key(r).  Its fragment reads put 32 consecutive lanes
-// on 32 consecutive rows at one chunk, and the LDS serves rows r and r+16 in
-// the same cycle: keying on r % 8 alone costs two conflict cycles per
-// ds_read_b128 (measured with SQ_LDS_BANK_CONFLICT), flipping bit 0 of the
-// key for rows 8-15 of every 16 removes them.
-__device__ __forceinline__ uint32_t il4_key(uint32_t row) {
-    return (row & 7u) ^ ((row >> 3) & 1u);
-}
-
-template <bool kFp8>
-__device__ __forceinline__ void il4_body(const GemmArgs& g, const IL4Buf buf0, const IL4Buf buf1) {
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
-    const uint32_t wn = wave & 1u;  // B rows (C columns) wn*128 .. +127
-
-    uint32_t tm, tn;
-    tile_of(blockIdx.x, g.grid, &tm, &tn);
-    const int32_t m0 = (int32_t)tm * kIL4Tile;
-    const int32_t n0 = (int32_t)tn * kIL4Tile;
-    const uint32_t kbytes = (uint32_t)g.K * (kFp8 ? 1u : 2u);
-    const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
-
-    // ---- HBM -> LDS.  A stage of an operand is 32 blocks of 8 rows; block b
-    // is one 16-byte load per lane (lane l -> row 8b + l/8, physical chunk
-    // l%8, which holds logical chunk (l%8) ^ il4_key(row)).  Wave w sends
-    // blocks w + 4j (j = 0..7) of A and of B: 16 loads per stage.  Its blocks
-    // all have the parity of w, so the key is a per-lane constant.
-    const uint32_t kc_lane = (lane & 7u) ^ il4_key((wave & 1u) * 8u + (lane >> 3));
-    uint32_t span_a, span_b;
-    {
-        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;  // rows past the edge read as zero
-        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
-        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
-        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
-    }
-    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
-    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
-    uint32_t voff_a[8], voff_b[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t row = (wave + 4u * j) * 8u + (lane >> 3);
-        voff_a[j] = row * g.lda_b + kc_lane * 16u;
-        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
-    }
-    // Load i (0-7: A block wave+4i, 8-15: B block wave+4(i-8)) of stage s into
-    // buffer d.  Lanes whose chunk lies at or past K (every lane, for a stage
-    // past the end) read zeros, which keeps every wait count constant.
-    auto send = [&](auto masked, const IL4Buf& d, uint32_t s, int i) {
-        const uint32_t koff = s * (uint32_t)kRowBytes;
-        const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
-        uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
-        if constexpr (decltype(masked)::value) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
-        if (i < 8)
-            load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
-        else
-            load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
-    };
-
-    // ---- LDS -> fragments.  For half h of a stage, the lane holds two
-    // 16-byte chunks of row (block base + l%32): logical chunks 4h + l/32 and
-    // 4h + 2 + l/32.  Lanes 0-31 and 32-63 thus cover the half's four chunks,
-    // identically for A and B.  Block bases are multiples of 32, so the
-    // swizzle key depends on the lane only.
-    const uint32_t r32 = lane & 31u;
-    const uint32_t hi = lane >> 5;
-    const uint32_t key = il4_key(r32);
-    uint32_t fo[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        fo[h][0] = r32 * kChunks + ((4u * h + hi) ^ key);
-        fo[h][1] = r32 * kChunks + ((4u * h + 2u + hi) ^ key);
-    }
-    const uint32_t arow = wm * 128u;
-    const uint32_t brow = wn * 128u;
-    // fragment f of half h: f = 0..3 A blocks, 4..7 B blocks; read c = 0, 1
-    auto read = [&](const IL4Buf& d, int h, int f, int c) -> i32x4 {
-        const HK_LDS i32x4* base = f < 4 ? d.a + (arow + 32u * (uint32_t)f) * kChunks
-                                         : d.b + (brow + 32u * (uint32_t)(f - 4)) * kChunks;
-        return base[fo[h][c]];
-    };
-
-    f32x16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-    // Matrix-core work of one half: MFMA number q of the half's list.
-    //  BF16: 32 MFMAs, K slice c = q / 16 outer, block (mb, nb) inner, so a
-    //        block's two slices are 16 instructions apart;
-    //  FP8:  16 MFMAs, one per block.
-    constexpr int kMfmaPerHalf = kFp8 ? 16 : 32;
-    auto mfma = [&](const i32x4 (&fr)[8][2], int q) {
-        const int blk = q & 15;
-        const int mb = blk >> 2, nb = blk & 3;
-        if constexpr (kFp8) {
-            acc[mb][nb] = mfma_fp8_32x32x64(
-                __builtin_shufflevector(fr[4 + nb][0], fr[4 + nb][1], 0, 1, 2, 3, 4, 5, 6, 7),
-                __builtin_shufflevector(fr[mb][0], fr[mb][1], 0, 1, 2, 3, 4, 5, 6, 7),
-                acc[mb][nb]);
-        } else {
-            const int c = q >> 4;
-            acc[mb][nb] = mfma_bf16_32x32x16(fr[4 + nb][c], fr[mb][c], acc[mb][nb]);
-        }
-    };
-
-    i32x4 fx[8][2], fy[8][2];  // fragments of the two halves in flight
-    // With one wave per SIMD, a memory instruction delays the wave's next
-    // matrix-core instruction, so the memory work of a half is spread evenly
-    // over its MFMAs (bursts of it measured slower).  Fragments are read in the
-    // order the MFMA list consumes them (A block 0, B blocks 0-3, A blocks
-    // 1-3), so that the next half's first MFMAs wait for only the first
-    // reads; the compiler waits for each fragment just before its first use.
-    auto rd = [&](i32x4 (&fr)[8][2], const IL4Buf& d, int h, int r) {
-        constexpr int kOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
-        // BF16 consumes slice 0 of every block before slice 1; FP8 needs both
-        // chunks of a block at once
-        const int f = kFp8 ? kOrder[r >> 1] : kOrder[r & 7];
-        const int c = kFp8 ? (r & 1) : (r >> 3);
-        fr[f][c] = read(d, h, f, c);
-    };
-    // memory slot of MFMA q: BF16 (32 per half) every other MFMA, FP8 (16
-    // per half, 64 cycles each) every MFMA
-    constexpr int kStep = kMfmaPerHalf / 16;
-    // Half 0 of stage t: MFMAs on fx; reads of half 1 into fy.
-    auto half0 = [&](const IL4Buf& cur) {
-#pragma unroll
-        for (int q = 0; q < kMfmaPerHalf; ++q) {
-            mfma(fx, q);
-            if (q % kStep == kStep - 1) rd(fy, cur, 1, q / kStep);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    // Half 1 of stage t: MFMAs on fy; the loads of stage t+2 and the reads of
-    // stage t+1's half 0 into fx.
-    auto half1 = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
-#pragma unroll
-        for (int q = 0; q < kMfmaPerHalf; ++q) {
-            mfma(fy, q);
-            if (q % kStep == kStep - 1) {
-                send(masked, cur, t + 2, q / kStep);
-                rd(fx, nxt, 0, q / kStep);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    auto stage = [&](auto masked, const IL4Buf& cur, const IL4Buf& nxt, uint32_t t) {
-        half0(cur);
-        wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
-        wait_vmcnt0();    // this wave's share of stage t+1 has landed
-        fenced_barrier();
-        half1(masked, cur, nxt, t);
-    };
-
-    // prologue: stages 0 and 1 in flight, stage 0 landed, F(0, 0) read
-    const std::true_type masked;
-    const std::false_type unmasked;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, buf0, 0, i);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, buf1, 1, i);
-    wait_vmcnt<16>();
-    fenced_barrier();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) rd(fx, buf0, 0, r);
-    // An even number of stages keeps the loop body free of branches; a stage
-    // past the end of K reads only zeros and adds exactly nothing.
-    // Stage pair (t, t+1) loads stages t+2 and t+3, all inside K while
-    // t + 4 <= the number of whole stages.
-    const uint32_t nk_whole = kbytes / kRowBytes;
-    uint32_t t = 0;
-    for (; t + 4 <= nk_whole; t += 2) {
-        stage(unmasked, buf0, buf1, t);
-        stage(unmasked, buf1, buf0, t + 1);
-    }
-    for (; t < nk; t += 2) {
-        stage(masked, buf0, buf1, t);
-        stage(masked, buf1, buf0, t + 1);
-    }
-    wait_all();  // no LDS write may outlive the workgroup
-
-    // ---- epilogue.  Block (mb, nb) of C^T: lane l holds C row
-    // m = arow + mb*32 + l%32 at columns n = brow + nb*32 + 8j + 4(l/32) + v,
-    // v = 0..3, in acc[mb][nb][4j + v].
-    const int32_t mbase = m0 + (int32_t)(arow + r32);
-    const int32_t nbase = n0 + (int32_t)(brow + hi * 4u);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        const int32_t m = mbase + mb * 32;
-        if (m < g.M) {
-            uint16_t* crow = g.C + (int64_t)m * g.ldc;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int32_t n = nbase + nb * 32 + j * 8;
-                    if (n < g.N) {
-                        f32x4 v = {acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1],
-                                   acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
-                        if constexpr (kFp8) v *= g.scale;
-                        store_bf16x4(crow + n, n, g.N, v, g.c_align);
-                    }
-                }
-        }
-    }
-}
-
-// BF16 form of the 4-wave interleave: v_mfma_f32_16x16x32_bf16, which on
-// gfx950 costs about 12% less energy per FLOP than the 32 x 32 shape when the
-// matrix cores are kept busy (the sustained clock of this power-bound GEMM
-// follows the energy per stage).  Each wave's 128 x 128 sub-tile is 8 x 8
-// blocks of 16 x 16 (256 accumulators per lane, pinned to the accumulation
-// registers); a stage's two K slices of 32 (chunks 0-3 and 4-7) take the
-// place of the halves above.  Fragment reads put 16 lanes on 16 rows at one
-// chunk, for which the key row % 8 is conflict-free.
+// BF16 form: v_mfma_f32_16x16x32_bf16, which on gfx950 costs about 12% less
+// energy per FLOP than the 32 x 32 shape when the matrix cores are kept busy
+// (the sustained clock of this power-bound GEMM follows the energy per
+// stage).  The two slices of a stage are its two K slices of 32 (chunks 0-3
+// and 4-7):
+//
+//   slice 0 of stage t:  64 MFMA on F(t, 0)  |  read F(t, 1)
+//   slice 1 of stage t:  64 MFMA on F(t, 1)  |  load stage t+2, read F(t+1, 0)
 //
 // Persistent: the grid has one workgroup per compute unit and workgroup b
 // computes tiles w = b, b + G, b + 2G, ... (G = grid size), which keeps the
@@ -730,6 +520,210 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
                 for (int nb = 0; nb < 8; ++nb) {
                     const int32_t n = ncol + nb * 16;
                     if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb], g.c_align);
+                }
+            }
+        }
+        if (w_next >= total) break;
+        w = w_next;
+        cur = nxt;
+        zero_acc();
+    }
+    wait_all();  // no LDS write may outlive the workgroup
+}
+
+// FP8 form of the persistent 4-wave interleave: v_mfma_scale_f32_16x16x128_f8f6f4
+// (E4M3 operands, unit block scales).  Same tile, LDS images, loads, tile
+// walk and pipeline across tiles as the BF16 form; a stage row of 128 bytes
+// is 128 E4M3 values, the whole K of one instruction, so a stage is one
+// MFMA per 16 x 16 block (64 per wave).  A block's fragment is the lane's
+// chunks g and g+4 (g = lane / 16) of row l%16, identically for A and B,
+// which pairs the same K values on both sides.
+//
+// A full stage of fragments (16 blocks x 32 bytes per lane) is half the
+// register file, so fragments are not double-buffered by stage.  Instead
+// the stage is split by A blocks and each fragment is refilled as soon as
+// its last reader has issued:
+//
+//   slice 0 of stage t:  MFMA A(t, 0-3) x B(t), A-block-major
+//                        | read A(t, 2-7)
+//   -- wait for this wave's reads and stage t+1's loads; workgroup barrier --
+//   slice 1 of stage t:  MFMA A(t, 4-7) x B(t), B-block-major
+//                        | after the last MFMA on B(t, n): read B(t+1, n);
+//                        | read A(t+1, 0-1); load stage t+2
+//
+// The barrier is the only one per stage, with the same meaning as in the
+// BF16 form.  A(t, 2) and A(t, 3) are read in slice 0 itself, 16 and 24
+// MFMAs ahead of their first use.
+__device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf0,
+                                             const IL4Buf buf1) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
+    const uint32_t wn = wave & 1u;  // B rows (C columns) wn*128 .. +127
+    const uint32_t total = (uint32_t)g.grid.tiles_m * (uint32_t)g.grid.tiles_n;
+    const uint32_t kbytes = (uint32_t)g.K;
+    const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+    const uint32_t nk_pad = (nk + 1u) & ~1u;  // stages run in pairs
+    const uint32_t nk_whole = kbytes / kRowBytes;
+
+    // ---- HBM -> LDS, as in the BF16 form: block b = 8 rows, lane l -> row
+    // 8b + l/8, physical chunk l%8 holding logical chunk (l%8) ^ (l/8); wave
+    // w sends blocks w + 4j (j = 0..7) of A and of B.
+    const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
+    uint32_t voff_a[8], voff_b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t row = (wave + 4u * j) * 8u + (lane >> 3);
+        voff_a[j] = row * g.lda_b + kc_lane * 16u;
+        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
+    }
+    struct Tile {
+        i32x4 ra, rb;
+        int32_t m0, n0;
+    };
+    auto tile = [&](uint32_t w) {
+        Tile t;
+        uint32_t tm = 0, tn = 0;
+        if (w < total) tile_of(w, g.grid, &tm, &tn);
+        t.m0 = (int32_t)tm * kIL4Tile;
+        t.n0 = (int32_t)tn * kIL4Tile;
+        const uint64_t sa = w < total ? (uint64_t)(g.M - t.m0) * g.lda_b : 0;
+        const uint64_t sb = w < total ? (uint64_t)(g.N - t.n0) * g.ldb_b : 0;
+        t.ra = make_rsrc_words(g.A + (int64_t)t.m0 * g.lda_b,
+                               (uint32_t)(sa > kOobOffset ? kOobOffset : sa));
+        t.rb = make_rsrc_words(g.B + (int64_t)t.n0 * g.ldb_b,
+                               (uint32_t)(sb > kOobOffset ? kOobOffset : sb));
+        return t;
+    };
+    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s, int i) {
+        const uint32_t koff = s * (uint32_t)kRowBytes;
+        const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
+        uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
+        if constexpr (decltype(masked)::value) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
+        if (i < 8)
+            load_lds_b128(tt.ra, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
+        else
+            load_lds_b128(tt.rb, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
+    };
+
+    // ---- LDS -> fragments: lane l holds row (block base + l%16), logical
+    // chunks g and g+4 (g = l/16) as one 32-byte operand.
+    const uint32_t r16 = lane & 15u;
+    const uint32_t g4 = lane >> 4;
+    const uint32_t fo0 = r16 * kChunks + ((0u + g4) ^ (r16 & 7u));
+    const uint32_t fo1 = r16 * kChunks + ((4u + g4) ^ (r16 & 7u));
+    const uint32_t arow = wm * 128u;
+    const uint32_t brow = wn * 128u;
+    auto rd_a = [&](const IL4Buf& d, int mb) -> i32x8 {
+        const HK_LDS i32x4* p = d.a + (arow + 16u * (uint32_t)mb) * kChunks;
+        return __builtin_shufflevector(p[fo0], p[fo1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto rd_b = [&](const IL4Buf& d, int nb) -> i32x8 {
+        const HK_LDS i32x4* p = d.b + (brow + 16u * (uint32_t)nb) * kChunks;
+        return __builtin_shufflevector(p[fo0], p[fo1], 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    f32x4 acc[8][8];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc_settle();  // the zeroed accumulators before the first MFMA reads them
+    };
+    // E8M0 exponent 127: block scale 1
+    const uint32_t one = 127u;
+    i32x8 fa[8], fb[8];
+    // C^T block (mb, nb): B block nb as the "A" operand, A block mb as "B"
+    auto mfma = [&](int mb, int nb) { mfma_fp8_16x16x128_pinned(acc[mb][nb], fb[nb], fa[mb], one); };
+
+    // slice 0 of stage t (in cur)
+    auto slice0 = [&](const IL4Buf& cur) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            mfma(q >> 3, q & 7);
+            if (q % 3 == 0 && q / 3 < 6) fa[2 + q / 3] = rd_a(cur, 2 + q / 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // slice 1 of stage t (in cur; stage t+1 in nxt), loading stage s of tile tt
+    auto slice1 = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
+                      const IL4Buf& nxt) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            mfma(4 + (q & 3), q >> 2);
+            if (q & 1) send(masked, tt, cur, s, q >> 1);
+            else if ((q & 3) == 0 && q > 0) fb[(q >> 2) - 1] = rd_b(nxt, (q >> 2) - 1);
+            else if (q == 2) fa[0] = rd_a(nxt, 0);
+            else if (q == 6) fa[1] = rd_a(nxt, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fb[7] = rd_b(nxt, 7);
+    };
+    auto stage = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
+                     const IL4Buf& nxt) {
+        slice0(cur);
+        wait_lgkmcnt0();  // A(t, 2-7) are in registers: this wave is done with stage t
+        wait_vmcnt0();    // this wave's share of stage t+1 has landed
+        fenced_barrier();
+        slice1(masked, tt, s, cur, nxt);
+    };
+
+    const std::true_type masked;
+    const std::false_type unmasked;
+    uint32_t w = blockIdx.x;
+    Tile cur = tile(w);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf0, 0, i);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf1, 1, i);
+    wait_vmcnt<16>();
+    fenced_barrier();
+    fa[0] = rd_a(buf0, 0);
+    fa[1] = rd_a(buf0, 1);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) fb[nb] = rd_b(buf0, nb);
+    zero_acc();
+
+    for (;;) {
+        const uint32_t w_next = w + gridDim.x;
+        const Tile nxt = tile(w_next);
+        uint32_t t = 0;
+        for (; t + 4 <= nk_whole; t += 2) {
+            stage(unmasked, cur, t + 2, buf0, buf1);
+            stage(unmasked, cur, t + 3, buf1, buf0);
+        }
+        // stages at or past the end of this tile's K load the next tile's
+        // first two (stage s of this tile is stage s - nk_pad of the next)
+        auto pick = [&](uint32_t s, uint32_t* s_out) {
+            const bool mine = s < nk_pad;
+            *s_out = mine ? s : s - nk_pad;
+            Tile r;
+            r.ra = mine ? cur.ra : nxt.ra;
+            r.rb = mine ? cur.rb : nxt.rb;
+            return r;
+        };
+        for (; t < nk_pad; t += 2) {
+            uint32_t s0, s1;
+            const Tile t0 = pick(t + 2, &s0);
+            stage(masked, t0, s0, buf0, buf1);
+            const Tile t1 = pick(t + 3, &s1);
+            stage(masked, t1, s1, buf1, buf0);
+        }
+        acc_settle();  // the last MFMA results before the epilogue reads them
+
+        // ---- epilogue: lane holds C[m][n..n+3] of block (mb, nb), times sA*sB
+        const int32_t mrow = cur.m0 + (int32_t)(arow + r16);
+        const int32_t ncol = cur.n0 + (int32_t)(brow + g4 * 4u);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const int32_t m = mrow + mb * 16;
+            if (m < g.M) {
+                uint16_t* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb) {
+                    const int32_t n = ncol + nb * 16;
+                    if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb] * g.scale, g.c_align);
                 }
             }
         }

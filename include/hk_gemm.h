@@ -67,14 +67,15 @@ typedef enum hk_dtype {
  *               its matrix-core cluster the other issues its memory cluster,
  *               and they swap at workgroup barriers;
  *   INTERLEAVE4 4 waves per CU, each interleaving its own loads with its
- *               matrix-core instructions;
+ *               matrix-core instructions; persistent (one workgroup per CU
+ *               walks its share of the output tiles);
  *   BASIC       a plain LDS-staged kernel with no alignment requirements,
  *               used for shapes or strides the fast schedules do not accept;
  *   INTERLEAVE8 8 waves per CU, each interleaving its own loads with its
  *               matrix-core instructions (BF16 only).
- * AUTO picks INTERLEAVE4 for BF16 and PINGPONG8 for FP8 (the faster of the
- * two on MI355X for each dtype) when the fast-path conditions hold (16-byte
- * aligned A and B, K, lda and ldb whole 16-byte chunks), else BASIC.
+ * AUTO picks INTERLEAVE4 (the fastest on MI355X for both dtypes) when the
+ * fast-path conditions hold (16-byte aligned A and B, K, lda and ldb whole
+ * 16-byte chunks), else BASIC.
  */
 typedef enum hk_schedule {
     HK_SCHEDULE_AUTO = 0,

@@ -151,8 +151,13 @@ def test_plan_fast_path_for_every_workload(M, N, K, tiles):
 
 def test_plan_fp8():
     p = _plan(hk.HK_DTYPE_FP8_E4M3, 8192, 8192, 8192)
-    assert p["kernel_name"] == "hk_gemm_pp8_fp8" and p["tile_k"] == 128
-    assert p["workgroups"] == 1024  # one workgroup per tile
+    assert p["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
+    assert p["kernel_name"] == "hk_gemm_il4_fp8" and p["tile_k"] == 128
+    assert p["workgroups"] == 256  # persistent: one workgroup per compute unit
+    assert p["threads"] == 256 and p["lds_bytes"] == 131072
+    # the ping-pong kernel on request: one workgroup per tile
+    p = _plan(hk.HK_DTYPE_FP8_E4M3, 8192, 8192, 8192, schedule="pingpong8")
+    assert p["kernel_name"] == "hk_gemm_pp8_fp8" and p["workgroups"] == 1024
 
 
 @pytest.mark.parametrize("K,lda,Aoff", [(60, 60, 0), (64, 66, 0), (64, 64, 2)])
@@ -165,7 +170,7 @@ def test_plan_falls_back_to_basic(K, lda, Aoff):
 
 def test_plan_fp8_fast_path_needs_16_byte_k():
     assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 8, lda=16, ldb=16)["schedule"] == hk.HK_SCHEDULE_BASIC
-    assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 32)["schedule"] == hk.HK_SCHEDULE_PINGPONG8
+    assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 32)["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
 
 
 def test_plan_zero_k_uses_the_fill_kernel():

@@ -140,6 +140,28 @@ def test_fast_schedules_ragged_integer(schedule, dtype, M, N, K):
     _full_check(dtype, A, B, M, N, K, K, K, exact=True, sa=sa, sb=sb, schedule=schedule)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("integer", [True, False])
+def test_persistent_tile_walk_full(dtype, integer):
+    """More output tiles than compute units, so that the persistent 4-wave
+    kernels carry their stage pipeline from one tile into the next; ragged
+    edges and a K tail (odd stage count), compared in full."""
+    M, N, K = 4359, 4352, 264 if dtype == "bf16" else 656
+    if dtype == "bf16":
+        dist = "int4" if integer else "normal"
+        A, B, sa, sb = _bf16(M, K, dist, 31), _bf16(N, K, dist, 32), 1.0, 1.0
+    else:
+        A, sa = gemm_inputs.fp8_matrix(M, K, 33, integer=integer)
+        B, sb = gemm_inputs.fp8_matrix(N, K, 34, integer=integer)
+        if integer:
+            sa, sb = 0.5, 4.0
+    p = hk.hk_gemm_plan(hk.HK_DTYPE_BF16 if dtype == "bf16" else hk.HK_DTYPE_FP8_E4M3,
+                        A.cuda(), B.cuda(), torch.empty(1, device="cuda"), M, N, K, K, K, N)
+    assert p["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
+    assert p["tiles_m"] * p["tiles_n"] > p["workgroups"]
+    _full_check(dtype, A, B, M, N, K, K, K, exact=integer, sa=sa, sb=sb)
+
+
 @pytest.mark.parametrize("group_m,window", [(1, 256), (3, 100), (16, 64), (8, 7)])
 def test_grid_parameters(group_m, window):
     M, N, K = 1300, 1100, 256
