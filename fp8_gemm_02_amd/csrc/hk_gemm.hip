@@ -62,6 +62,18 @@ hk_gemm_i8_bf16(hk::GemmArgs g) {
     hk::i8_body(g, buf0, buf1);
 }
 
+extern "C" __global__ void __launch_bounds__(hk::kSTThreads)
+hk_gemm_st4_bf16(hk::GemmArgs g) {
+    __shared__ hk::i32x4 ring[hk::kSTStages * 2 * hk::kSTStageI4];
+    hk::st4_body<false>(g, (HK_LDS hk::i32x4*)ring);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kSTThreads)
+hk_gemm_st4_fp8(hk::GemmArgs g) {
+    __shared__ hk::i32x4 ring[hk::kSTStages * 2 * hk::kSTStageI4];
+    hk::st4_body<true>(g, (HK_LDS hk::i32x4*)ring);
+}
+
 extern "C" __global__ void __launch_bounds__(hk::kBasicThreads)
 hk_gemm_basic_bf16(hk::GemmArgs g) {
     __shared__ hk::i32x4 sA[hk::kBasicStageI4], sB[hk::kBasicStageI4];
@@ -128,7 +140,7 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
     if (dtype != HK_DTYPE_BF16 && dtype != HK_DTYPE_FP8_E4M3) return HK_ERROR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return HK_ERROR_INVALID_VALUE;
     if (opts) {
-        if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_INTERLEAVE8)
+        if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_SMALLTILE)
             return HK_ERROR_INVALID_VALUE;
         if (opts->grid_order < HK_GRID_AUTO || opts->grid_order > HK_GRID_XCD)
             return HK_ERROR_INVALID_VALUE;
@@ -166,12 +178,17 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     const bool fast_ok = aligned(A, 16) && aligned(B, 16) && K % chunk == 0 &&
                          lda % chunk == 0 && ldb % chunk == 0 &&
                          lda_b * hk::kPP8Tile < kMaxRowBytes && ldb_b * hk::kPP8Tile < kMaxRowBytes;
-    // Measured on MI355X at 8192^3: the 4-wave interleave is the faster
-    // kernel for both dtypes.
-    if (sched == HK_SCHEDULE_AUTO) sched = fast_ok ? HK_SCHEDULE_INTERLEAVE4 : HK_SCHEDULE_BASIC;
-    if ((sched == HK_SCHEDULE_PINGPONG8 || sched == HK_SCHEDULE_INTERLEAVE4 ||
-         sched == HK_SCHEDULE_INTERLEAVE8) && !fast_ok)
-        return HK_ERROR_NOT_SUPPORTED;
+    // Measured on MI355X: the 4-wave interleave is the faster kernel for both
+    // dtypes at 8192^3; outputs with few 256 x 256 tiles (at most one per
+    // four compute units) run faster on 128 x 128 tiles with more stages in
+    // flight.
+    const int32_t cus = current_cu_count();
+    if (sched == HK_SCHEDULE_AUTO) {
+        const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+        sched = !fast_ok ? HK_SCHEDULE_BASIC
+                         : (tiles256 * 4 <= cus ? HK_SCHEDULE_SMALLTILE : HK_SCHEDULE_INTERLEAVE4);
+    }
+    if (sched != HK_SCHEDULE_BASIC && !fast_ok) return HK_ERROR_NOT_SUPPORTED;
     if (sched == HK_SCHEDULE_INTERLEAVE8 && dtype != HK_DTYPE_BF16) return HK_ERROR_NOT_SUPPORTED;
 
     const bool fp8 = dtype == HK_DTYPE_FP8_E4M3;
@@ -187,6 +204,12 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
         p->lds_bytes = 4 * hk::kIL4StageI4 * 16;
         p->kernel = (const void*)hk_gemm_i8_bf16;
         p->name = "hk_gemm_i8_bf16";
+    } else if (sched == HK_SCHEDULE_SMALLTILE) {
+        p->tile = hk::kSTTile;
+        p->threads = hk::kSTThreads;
+        p->lds_bytes = hk::kSTStages * 2 * hk::kSTStageI4 * 16;
+        p->kernel = fp8 ? (const void*)hk_gemm_st4_fp8 : (const void*)hk_gemm_st4_bf16;
+        p->name = fp8 ? "hk_gemm_st4_fp8" : "hk_gemm_st4_bf16";
     } else if (sched == HK_SCHEDULE_INTERLEAVE4) {
         p->tile = hk::kIL4Tile;
         p->threads = hk::kIL4Threads;
@@ -207,7 +230,6 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     p->tiles_n = (N + p->tile - 1) / p->tile;
     if (p->tiles_m * p->tiles_n > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
 
-    const int32_t cus = current_cu_count();
     p->grid = p->tiles_m * p->tiles_n;
     // the 4-wave kernels are persistent: one workgroup per compute unit
     if (sched == HK_SCHEDULE_INTERLEAVE4 && p->grid > cus) p->grid = cus;

@@ -904,6 +904,160 @@ __device__ __forceinline__ void i8_body(const GemmArgs& g, const IL4Buf buf0, co
     }
 }
 
+// --------------------------------------------------------- small outputs
+//
+// For outputs with few 256 x 256 tiles, where the GEMM is bound by the
+// latency of the first loads rather than by the matrix cores: 128 x 128
+// tiles (four times as many workgroups), 4 waves in a 2 x 2 arrangement of
+// 64 x 64 sub-tiles (4 x 4 blocks of 16 x 16), and a ring of four stage
+// buffers (4 x 32 KiB) with three stages in flight ahead of the one being
+// computed.  K up to three stages (192 BF16 or 384 E4M3) is fetched before
+// the first matrix-core instruction; one barrier per stage:
+//
+//   stage t:  wait for this wave's share of stage t; workgroup barrier
+//             (stage t is visible, buffer (t-1) % 4 is free);
+//             load stage t+3 into buffer (t+3) % 4;
+//             read and compute stage t
+//
+// Loads, LDS image rows and fragment layout are those of the 4-wave
+// kernels (direct HBM -> LDS loads, key row % 8).
+constexpr int kSTTile = 128;
+constexpr int kSTThreads = 256;
+constexpr int kSTStages = 4;
+constexpr int kSTStageI4 = kSTTile * kChunks;  // 16-byte chunks per operand per stage
+
+template <bool kFp8>
+__device__ __forceinline__ void st4_body(const GemmArgs& g, HK_LDS i32x4* ring) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wm = wave >> 1;  // A rows wm*64 .. +63
+    const uint32_t wn = wave & 1u;  // B rows (C columns) wn*64 .. +63
+
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, g.grid, &tm, &tn);
+    const int32_t m0 = (int32_t)tm * kSTTile;
+    const int32_t n0 = (int32_t)tn * kSTTile;
+    const uint32_t kbytes = (uint32_t)g.K * (kFp8 ? 1u : 2u);
+    const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+
+    // ---- HBM -> LDS: an operand's stage is 16 blocks of 8 rows (lane l ->
+    // row 8b + l/8, physical chunk l%8 holding logical chunk (l%8) ^ (l/8));
+    // wave w sends blocks w + 4j (j = 0..3) of A and of B: 8 loads per stage.
+    const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
+    uint32_t span_a, span_b;
+    {
+        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;  // rows past the edge read as zero
+        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
+        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
+        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
+    }
+    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
+    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
+    uint32_t voff_a[4], voff_b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t row = (wave + 4u * j) * 8u + (lane >> 3);
+        voff_a[j] = row * g.lda_b + kc_lane * 16u;
+        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
+    }
+    auto buf_a = [&](uint32_t s) { return ring + (s % kSTStages) * 2u * kSTStageI4; };
+    auto buf_b = [&](uint32_t s) { return ring + ((s % kSTStages) * 2u + 1u) * kSTStageI4; };
+    // the 8 loads of stage s; lanes whose chunk lies at or past K (every
+    // lane, for a stage past the end) read zeros, which keeps the wait
+    // counts constant
+    auto issue = [&](uint32_t s) {
+        const uint32_t koff = s * (uint32_t)kRowBytes;
+        const bool in_k = koff + kc_lane * 16u < kbytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t blk = wave + 4u * j;
+            load_lds_b128(rsrc_a, (HK_LDS void*)(buf_a(s) + blk * 64u), in_k ? voff_a[j] : kOobOffset,
+                          koff);
+            load_lds_b128(rsrc_b, (HK_LDS void*)(buf_b(s) + blk * 64u), in_k ? voff_b[j] : kOobOffset,
+                          koff);
+        }
+    };
+
+    // ---- fragments: lane l holds row (block base + l%16), logical chunks
+    // g and g+4 (g = l/16): the two K slices of 32 for BF16, the whole 128
+    // E4M3 of one MFMA for FP8
+    const uint32_t r16 = lane & 15u;
+    const uint32_t g4 = lane >> 4;
+    const uint32_t fo0 = r16 * kChunks + ((0u + g4) ^ (r16 & 7u));
+    const uint32_t fo1 = r16 * kChunks + ((4u + g4) ^ (r16 & 7u));
+    const uint32_t arow = wm * 64u;
+    const uint32_t brow = wn * 64u;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (uint32_t s = 0; s < kSTStages - 1; ++s) issue(s);
+    for (uint32_t t = 0; t < nk; ++t) {
+        wait_vmcnt<16>();  // stage t landed; stages t+1, t+2 may be in flight
+        wait_lgkmcnt0();   // this wave's reads of stage t-1 are done
+        fenced_barrier();
+        issue(t + kSTStages - 1);
+        const HK_LDS i32x4* pa = buf_a(t) + arow * kChunks;
+        const HK_LDS i32x4* pb = buf_b(t) + brow * kChunks;
+        i32x4 a0[4], a1[4], b0[4], b1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a0[i] = pa[i * 16 * kChunks + fo0];
+            b0[i] = pb[i * 16 * kChunks + fo0];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a1[i] = pa[i * 16 * kChunks + fo1];
+            b1[i] = pb[i * 16 * kChunks + fo1];
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                if constexpr (kFp8) {
+                    acc[mb][nb] = mfma_fp8_16x16x128(
+                        __builtin_shufflevector(b0[nb], b1[nb], 0, 1, 2, 3, 4, 5, 6, 7),
+                        __builtin_shufflevector(a0[mb], a1[mb], 0, 1, 2, 3, 4, 5, 6, 7),
+                        acc[mb][nb]);
+                } else {
+                    acc[mb][nb] = mfma_bf16_16x16x32(b0[nb], a0[mb], acc[mb][nb]);
+                }
+            }
+        if constexpr (!kFp8) {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[mb][nb] = mfma_bf16_16x16x32(b1[nb], a1[mb], acc[mb][nb]);
+        }
+    }
+    wait_all();  // no LDS write may outlive the workgroup
+
+    // ---- epilogue: lane holds C[m][n..n+3] of block (mb, nb)
+    const int32_t mrow = m0 + (int32_t)(arow + r16);
+    const int32_t ncol = n0 + (int32_t)(brow + g4 * 4u);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int32_t m = mrow + mb * 16;
+        if (m < g.M) {
+            uint16_t* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int32_t n = ncol + nb * 16;
+                if (n < g.N) {
+                    f32x4 v = acc[mb][nb];
+                    if constexpr (kFp8) v *= g.scale;
+                    store_bf16x4(crow + n, n, g.N, v, g.c_align);
+                }
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------------- fallback
 
 constexpr int kBasicTile = 64;

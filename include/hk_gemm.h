@@ -72,17 +72,21 @@ typedef enum hk_dtype {
  *   BASIC       a plain LDS-staged kernel with no alignment requirements,
  *               used for shapes or strides the fast schedules do not accept;
  *   INTERLEAVE8 8 waves per CU, each interleaving its own loads with its
- *               matrix-core instructions (BF16 only).
- * AUTO picks INTERLEAVE4 (the fastest on MI355X for both dtypes) when the
- * fast-path conditions hold (16-byte aligned A and B, K, lda and ldb whole
- * 16-byte chunks), else BASIC.
+ *               matrix-core instructions (BF16 only);
+ *   SMALLTILE   128 x 128 tiles with four K stages in flight, for outputs
+ *               too small to give every CU a 256 x 256 tile.
+ * AUTO, when the fast-path conditions hold (16-byte aligned A and B, K, lda
+ * and ldb whole 16-byte chunks), picks SMALLTILE if the output has at most
+ * one 256 x 256 tile per four compute units and INTERLEAVE4 (the fastest on
+ * MI355X at large sizes for both dtypes) otherwise; else BASIC.
  */
 typedef enum hk_schedule {
     HK_SCHEDULE_AUTO = 0,
     HK_SCHEDULE_PINGPONG8 = 1,
     HK_SCHEDULE_INTERLEAVE4 = 2,
     HK_SCHEDULE_BASIC = 3,
-    HK_SCHEDULE_INTERLEAVE8 = 4
+    HK_SCHEDULE_INTERLEAVE8 = 4,
+    HK_SCHEDULE_SMALLTILE = 5
 } hk_schedule;
 
 /*

@@ -132,7 +132,7 @@ def _plan(dtype, M, N, K, lda=None, ldb=None, ldc=None, A=FAKE, B=FAKE, C=FAKE, 
     return hk.hk_gemm_plan(dtype, A, B, C, M, N, K, lda or K, ldb or K, ldc or N, **kw)
 
 
-@pytest.mark.parametrize("M,N,K,tiles", [(256, 256, 256, (1, 1)), (4096, 4096, 4096, (16, 16)),
+@pytest.mark.parametrize("M,N,K,tiles", [(4096, 4096, 4096, (16, 16)),
                                          (8192, 8192, 8192, (32, 32)),
                                          (8192, 28672, 8192, (32, 112)),
                                          (8191, 28670, 8200, (32, 112))])
@@ -147,6 +147,31 @@ def test_plan_fast_path_for_every_workload(M, N, K, tiles):
     assert p["threads"] == 256 and p["lds_bytes"] == 131072
     assert p["tile_k"] == 64
     assert p["grid_order"] == hk.HK_GRID_XCD
+
+
+@pytest.mark.parametrize("dtype,name", [(hk.HK_DTYPE_BF16, "hk_gemm_st4_bf16"),
+                                        (hk.HK_DTYPE_FP8_E4M3, "hk_gemm_st4_fp8")])
+@pytest.mark.parametrize("M,N,tiles", [(256, 256, (2, 2)), (2048, 2048, (16, 16)),
+                                       (300, 4000, (3, 32))])
+def test_plan_small_outputs_use_128_tiles(dtype, name, M, N, tiles):
+    # at most one 256 x 256 tile per four compute units
+    p = _plan(dtype, M, N, 256)
+    assert p["schedule"] == hk.HK_SCHEDULE_SMALLTILE and p["kernel_name"] == name
+    assert (p["tile_m"], p["tile_n"]) == (128, 128)
+    assert (p["tiles_m"], p["tiles_n"]) == tiles
+    assert p["workgroups"] == tiles[0] * tiles[1]  # one workgroup per tile
+    assert p["threads"] == 256 and p["lds_bytes"] == 131072
+
+
+def test_plan_small_tiles_on_request():
+    p = _plan(hk.HK_DTYPE_BF16, 8192, 8192, 8192, schedule="smalltile")
+    assert p["kernel_name"] == "hk_gemm_st4_bf16" and p["workgroups"] == 64 * 64
+
+
+def test_plan_small_output_threshold():
+    # 64 tiles of 256 x 256 on 256 compute units: small; 65: the 4-wave kernel
+    assert _plan(hk.HK_DTYPE_BF16, 2048, 2048, 64)["schedule"] == hk.HK_SCHEDULE_SMALLTILE
+    assert _plan(hk.HK_DTYPE_BF16, 2048, 2049, 64)["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
 
 
 def test_plan_fp8():
@@ -170,7 +195,7 @@ def test_plan_falls_back_to_basic(K, lda, Aoff):
 
 def test_plan_fp8_fast_path_needs_16_byte_k():
     assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 8, lda=16, ldb=16)["schedule"] == hk.HK_SCHEDULE_BASIC
-    assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 32)["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
+    assert _plan(hk.HK_DTYPE_FP8_E4M3, 64, 64, 32)["schedule"] == hk.HK_SCHEDULE_SMALLTILE
 
 
 def test_plan_zero_k_uses_the_fill_kernel():
@@ -194,6 +219,7 @@ def test_plan_rejects_huge_strides():
     ("interleave8", hk.HK_DTYPE_BF16, "hk_gemm_i8_bf16", 512),
     ("pingpong8", hk.HK_DTYPE_FP8_E4M3, "hk_gemm_pp8_fp8", 512)])
 def test_plan_explicit_schedules(schedule, dtype, name, threads):
+    # a large output on request of a schedule (small tiles tested above)
     p = _plan(dtype, 8192, 8192, 8192, schedule=schedule)
     assert p["kernel_name"] == name and p["threads"] == threads
     assert (p["tile_m"], p["tile_n"]) == (256, 256) and p["lds_bytes"] == 131072

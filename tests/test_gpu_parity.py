@@ -110,7 +110,7 @@ def test_fp8_ragged_full(M, N, K, integer):
     _full_check("fp8", A, B, M, N, K, K, K, exact=integer, sa=sa, sb=sb)
 
 
-@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "basic"])
+@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "smalltile", "basic"])
 @pytest.mark.parametrize("grid_order", ["row_major", "xcd"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_every_variant(schedule, grid_order, dtype):
@@ -124,7 +124,7 @@ def test_every_variant(schedule, grid_order, dtype):
                 grid_order=grid_order)
 
 
-@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "interleave8"])
+@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "interleave8", "smalltile"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("M,N,K", [(513, 769, 1040), (256, 256, 128), (300, 40, 16)])
 def test_fast_schedules_ragged_integer(schedule, dtype, M, N, K):
