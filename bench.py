@@ -1,15 +1,17 @@
 """Benchmark: BF16 GEMM C = A * B^T at 8192^3 on one MI355X (TFLOP/s, % of 2.5 PF).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--schedule S] [--grid-order G] [--no-cpu-baseline]
+                    [--schedule S] [--grid-order G] [--no-cpu-baseline] [--no-flush]
 
 A step is one call of the whole path (hk_gemm_bf16 / hk_gemm_fp8 through the
 C ABI) on inputs already resident in HBM.  W untimed steps, then exactly K
 timed steps bracketed by device synchronisation; `value` is 2*M*N*K*steps /
 elapsed.  Each launch is also bracketed by HIP events on its own stream, and
-the mean event duration gives `roofline.achieved`.  The CPU baseline times the
-FP64 oracle on a bounded sample of output rows on the host cores.  Prints one
-JSON line.
+the mean event duration gives `roofline.achieved`.  After the timed region,
+launches preceded by a 1 GiB fill (which evicts L2 and the last-level cache)
+are timed the same way and reported as `flushed_kernel_ms`.  The CPU baseline
+times the FP64 oracle on a bounded sample of output rows on the host cores.
+`inputs` holds the SHA-256 of the operand bytes.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -40,8 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--extra", action="store_true",
-                    help="also time each launch after an L2/LLC flush and report it")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the per-launch timing after an L2/LLC flush")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the GEMM, run one plain device-to-device copy of BYTES "
                          "bytes (torch copy_) 5 times; the HBM byte counters read on it "
@@ -114,8 +116,19 @@ def cpu_baseline(w, x, seconds: float):
     t = run(rows)
     flops = 2.0 * rows * w.N * w.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d of %d output rows (all %d columns, K=%d), FP64 scalar oracle, %.1f s"
                       % (rows, w.M, w.N, w.K, t)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -145,6 +158,8 @@ def main():
     plan = hk.hk_gemm_plan(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, **opts)
     stream = torch.cuda.Stream()
     sa, sb = x["scale_a"], x["scale_b"]
+    inputs = {"A_sha256": gemm_inputs.sha256(x["A"]), "B_sha256": gemm_inputs.sha256(x["B"]),
+              "scale_a": sa, "scale_b": sb}
 
     def step():
         hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, sa, sb,
@@ -198,6 +213,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS[w.dtype], 2),
         "kernel_ms": {"mean": round(mean_ms, 4), "median": round(durs_ms[len(durs_ms) // 2], 4),
                       "min": round(durs_ms[0], 4), "max": round(durs_ms[-1], 4)},
+        "inputs": inputs,
     }
     tr = traffic_from_profiles(plan["kernel_name"], w.name)
     # The binding roofline follows the arithmetic intensity: below the ridge
@@ -218,8 +234,9 @@ def main():
                             "algorithmic_flops_per_launch": flops,
                             "algorithmic_bytes_per_launch": w.algorithmic_bytes})
 
-    if a.extra:
-        # per-launch time after flushing L2 and the last-level cache
+    if not a.no_flush:
+        # per-launch time after flushing L2 and the last-level cache (a 1 GiB
+        # fill between launches, outside the events)
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         fl = []
         for _ in range(max(5, a.steps // 5)):
@@ -233,7 +250,8 @@ def main():
             torch.cuda.synchronize()
             fl.append(s.elapsed_time(e))
         fl.sort()
-        out["flushed_kernel_ms_median"] = round(fl[len(fl) // 2], 4)
+        out["flushed_kernel_ms"] = {"median": round(fl[len(fl) // 2], 4), "min": round(fl[0], 4),
+                                    "max": round(fl[-1], 4), "launches": len(fl)}
         del flush
 
     if not a.no_cpu_baseline:

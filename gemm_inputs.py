@@ -68,6 +68,9 @@ WORKLOADS = {
         Workload("bf16_mlp", 3, 8192, 28672, 8192, "bf16", "normal002"),
         Workload("bf16_mlp_ragged", 3, 8191, 28670, 8200, "bf16", "normal002"),
         Workload("fp8_8192", 4, 8192, 8192, 8192, "fp8", "fp8_normal"),
+        # one GPU's share of the MLP shape split over 8 GPUs along N (448
+        # tiles of 256 x 256: 1.75 windows of 256 co-resident workgroups)
+        Workload("bf16_mlp_shard8", 3, 8192, 3584, 8192, "bf16", "normal002"),
     ]
 }
 
