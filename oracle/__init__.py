@@ -63,6 +63,14 @@ def _load():
     lib.oracle_bf16_decode.restype = f64
     lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_decode.restype = f64
+    lib.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_decode.restype = f64
+    lib.oracle_gemm_mx.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                   i64, i32]
+    lib.oracle_gemm_mx.restype = i32
+    lib.oracle_gemm_mx_sampled.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                           vp, vp, i64, vp, vp, i32]
+    lib.oracle_gemm_mx_sampled.restype = i32
     _lib = lib
     return lib
 
@@ -146,6 +154,66 @@ def gemm_sampled(dtype, A: np.ndarray, B: np.ndarray, M: int, N: int, K: int,
     if rc != 0:
         raise ValueError("oracle_gemm_sampled rejected its arguments")
     return c, s
+
+
+def _mx_operands(A, B, SA, SB, M, N, K, lda, ldb, ldsa, ldsb):
+    nb = (K + 31) // 32
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldsa = nb if ldsa is None else ldsa
+    ldsb = nb if ldsb is None else ldsb
+    A, B = _as_bits(A, E4M3), _as_bits(B, E4M3)
+    SA, SB = _as_bits(SA, E4M3), _as_bits(SB, E4M3)  # E8M0 scale bytes
+    if M > 0 and K > 0 and (A.size < (M - 1) * lda + K or SA.size < (M - 1) * ldsa + nb):
+        raise ValueError("A or its scales too small")
+    if N > 0 and K > 0 and (B.size < (N - 1) * ldb + K or SB.size < (N - 1) * ldsb + nb):
+        raise ValueError("B or its scales too small")
+    return A, B, SA, SB, lda, ldb, ldsa, ldsb
+
+
+def gemm_mx(A: np.ndarray, B: np.ndarray, SA: np.ndarray, SB: np.ndarray, M: int, N: int,
+            K: int, lda: int | None = None, ldb: int | None = None, ldsa: int | None = None,
+            ldsb: int | None = None, threads: int | None = None, want_s: bool = True):
+    """Full MXFP8 oracle product.
+
+    A, B: E4M3 bytes with row strides lda, ldb.  SA, SB: E8M0 scale bytes, one
+    per 32 K-elements of a row, with row strides ldsa, ldsb (default ceil(K/32)).
+    Returns (C bits (M, N) uint16, S (M, N) float64 or None).
+    """
+    A, B, SA, SB, lda, ldb, ldsa, ldsb = _mx_operands(A, B, SA, SB, M, N, K, lda, ldb, ldsa, ldsb)
+    C = np.zeros((M, N), dtype=np.uint16)
+    S = np.zeros((M, N), dtype=np.float64) if want_s else None
+    rc = _load().oracle_gemm_mx(A.ctypes.data, B.ctypes.data, SA.ctypes.data, SB.ctypes.data,
+                                C.ctypes.data, S.ctypes.data if S is not None else None,
+                                M, N, K, lda, ldb, ldsa, ldsb, N, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm_mx rejected its arguments")
+    return C, S
+
+
+def gemm_mx_sampled(A, B, SA, SB, M: int, N: int, K: int, rows, cols, lda=None, ldb=None,
+                    ldsa=None, ldsb=None, threads: int | None = None):
+    """MXFP8 oracle entries C[rows[p], cols[p]] and their magnitude sums."""
+    A, B, SA, SB, lda, ldb, ldsa, ldsb = _mx_operands(A, B, SA, SB, M, N, K, lda, ldb, ldsa, ldsb)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows/cols shape mismatch")
+    n = rows.size
+    c = np.zeros(n, dtype=np.uint16)
+    s = np.zeros(n, dtype=np.float64)
+    rc = _load().oracle_gemm_mx_sampled(A.ctypes.data, B.ctypes.data, SA.ctypes.data,
+                                        SB.ctypes.data, M, N, K, lda, ldb, ldsa, ldsb,
+                                        rows.ctypes.data, cols.ctypes.data, n, c.ctypes.data,
+                                        s.ctypes.data, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_gemm_mx_sampled rejected its arguments")
+    return c, s
+
+
+def e8m0_decode(x: int) -> float:
+    """Decode one E8M0 scale byte: 2^(x - 127), NaN for 255."""
+    return _load().oracle_e8m0_decode(int(x))
 
 
 def bf16_round(x) -> np.ndarray:

@@ -244,3 +244,128 @@ int oracle_num_threads_available(void)
     return 1;
 #endif
 }
+
+/*
+ * ---------------------------------------------------------------- MXFP8
+ *
+ * Block-scaled FP8 ("MXFP8", the format of the pages' 5.0 PF FP8 peak in "How
+ * to make AMD GPUs go brrr", section "AMD CDNA GPU structure").  The pages
+ * name the format only; its definition is the OCP Microscaling (MX) Formats
+ * specification v1.0: along K, every block of 32 consecutive elements of a
+ * row shares one scale X in E8M0, an 8-bit biased exponent (bias 127) with
+ * value 2^(x - 127), where x = 255 encodes NaN.  The elements are E4M3FN, and
+ * an element's value is X * dec(element).  The product is then
+ *
+ *     C[i][j] = RNE_bf16( sum_k XA[i][k/32] dec(A[i][k]) * XB[j][k/32] dec(B[j][k]) )
+ *
+ * with XA stored as an M x ceil(K/32) byte array of row stride ldsa and XB as
+ * N x ceil(K/32) of row stride ldsb (a last block shorter than 32 keeps its
+ * scale).  Each term is exact in double (the element product has at most 8
+ * significant bits, the scales are powers of two far inside double's range),
+ * and the sum, the magnitude sum and the rounding follow the plain product
+ * above: ascending k from +0.0, one rounding per add, one final rounding.
+ */
+double oracle_e8m0_decode(uint8_t x)
+{
+    if (x == 255)
+        return NAN;
+    return ldexp(1.0, (int)x - 127);
+}
+
+static void dot_one_mx(const uint8_t *A, const uint8_t *B, const uint8_t *SA,
+                       const uint8_t *SB, int64_t i, int64_t j, int64_t K, int64_t lda,
+                       int64_t ldb, int64_t ldsa, int64_t ldsb, const double *tab,
+                       const double *xtab, double *c_out, double *s_out)
+{
+    double acc = 0.0, mag = 0.0;
+    int64_t k;
+    for (k = 0; k < K; ++k) {
+        double a = xtab[SA[i * ldsa + k / 32]] * tab[A[i * lda + k]];
+        double b = xtab[SB[j * ldsb + k / 32]] * tab[B[j * ldb + k]];
+        double p = a * b;
+        acc = acc + p;
+        mag = mag + fabs(p);
+    }
+    *c_out = acc;
+    *s_out = mag;
+}
+
+static int check_args_mx(const void *A, const void *B, const void *SA, const void *SB,
+                         int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                         int64_t ldsa, int64_t ldsb)
+{
+    int64_t nb = (K + 31) / 32;
+    if (check_args(ORACLE_E4M3, A, B, M, N, K, lda, ldb))
+        return 1;
+    if (K > 0 && ((M > 0 && (SA == NULL || ldsa < nb)) || (N > 0 && (SB == NULL || ldsb < nb))))
+        return 1;
+    return 0;
+}
+
+static void mx_tables(double *tab, double *xtab)
+{
+    int t;
+    for (t = 0; t < 256; ++t) {
+        tab[t] = oracle_e4m3_decode((uint8_t)t);
+        xtab[t] = oracle_e8m0_decode((uint8_t)t);
+    }
+}
+
+/* Full MXFP8 product; C, S and the return value as for oracle_gemm. */
+int oracle_gemm_mx(const uint8_t *A, const uint8_t *B, const uint8_t *SA, const uint8_t *SB,
+                   uint16_t *C, double *S, int64_t M, int64_t N, int64_t K, int64_t lda,
+                   int64_t ldb, int64_t ldsa, int64_t ldsb, int64_t ldc, int nthreads)
+{
+    double tab[256], xtab[256];
+    int64_t i;
+
+    if (check_args_mx(A, B, SA, SB, M, N, K, lda, ldb, ldsa, ldsb) || ldc < N ||
+        (M > 0 && N > 0 && C == NULL))
+        return 1;
+    mx_tables(tab, xtab);
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (i = 0; i < M; ++i) {
+        int64_t j;
+        for (j = 0; j < N; ++j) {
+            double c, m;
+            dot_one_mx(A, B, SA, SB, i, j, K, lda, ldb, ldsa, ldsb, tab, xtab, &c, &m);
+            C[i * ldc + j] = oracle_bf16_round(c);
+            if (S)
+                S[i * N + j] = m;
+        }
+    }
+    return 0;
+}
+
+/* Selected entries of the MXFP8 product, as oracle_gemm_sampled. */
+int oracle_gemm_mx_sampled(const uint8_t *A, const uint8_t *B, const uint8_t *SA,
+                           const uint8_t *SB, int64_t M, int64_t N, int64_t K, int64_t lda,
+                           int64_t ldb, int64_t ldsa, int64_t ldsb, const int64_t *rows,
+                           const int64_t *cols, int64_t n, uint16_t *c_out, double *s_out,
+                           int nthreads)
+{
+    double tab[256], xtab[256];
+    int64_t p;
+
+    if (check_args_mx(A, B, SA, SB, M, N, K, lda, ldb, ldsa, ldsb) || n < 0)
+        return 1;
+    for (p = 0; p < n; ++p)
+        if (rows[p] < 0 || rows[p] >= M || cols[p] < 0 || cols[p] >= N)
+            return 1;
+    mx_tables(tab, xtab);
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (p = 0; p < n; ++p) {
+        double c, m;
+        dot_one_mx(A, B, SA, SB, rows[p], cols[p], K, lda, ldb, ldsa, ldsb, tab, xtab, &c, &m);
+        c_out[p] = oracle_bf16_round(c);
+        if (s_out)
+            s_out[p] = m;
+    }
+    return 0;
+}

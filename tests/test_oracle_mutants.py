@@ -3,8 +3,10 @@
 Each case below plants one plausible mistake in a copy of oracle.c (a dropped
 term, float accumulation, a transposed operand, a wrong e4m3 bias or sign,
 rounding twice, the wrong tie rule, a lost scale, a lost subnormal clamp, an
-ignored row stride), builds the copy on the CPU in a temporary directory, and
-runs the pins of test_oracle.py against it.  At least one pin must fail for
+ignored row stride; for MXFP8: the wrong block size or block index, the wrong
+scale bias, swapped scale arrays, a NaN scale read as finite, an ignored scale
+stride), builds the copy on the CPU in a temporary directory, and
+runs the pins of test_oracle.py and test_oracle_mx.py against it.  At least one pin must fail for
 every mutant.  The oracle itself is never modified.
 """
 import ctypes
@@ -15,6 +17,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_mx as mx_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -30,6 +33,12 @@ MUTANTS = {
     "ties_away": ("r = rint(ax / q) * q;", "r = round(ax / q) * q;"),
     "lost_scale": ("*c_out = acc * s;", "*c_out = acc;"),
     "no_subnormal_clamp": ("E = -126;", "E = E;"),
+    "mx_block_of_16": ("k / 32]", "k / 16]"),
+    "mx_block_off_by_one": ("SA[i * ldsa + k / 32]", "SA[i * ldsa + (k + 1) / 32]"),
+    "mx_scale_bias_128": ("ldexp(1.0, (int)x - 127)", "ldexp(1.0, (int)x - 128)"),
+    "mx_scales_swapped": ("xtab[SA[i * ldsa + k / 32]]", "xtab[SB[i * ldsb + k / 32]]"),
+    "mx_nan_scale_ignored": ("if (x == 255)\n        return NAN;", "if (x == 255)\n        return 1.0;"),
+    "mx_ignored_ldsa": ("SA[i * ldsa + k / 32]", "SA[i * ((K + 31) / 32) + k / 32]"),
 }
 
 PINS = [
@@ -45,6 +54,12 @@ PINS = [
     pins.test_identity_B_bf16,
     pins.test_non_square_orientation,
     pins.test_strided_equals_packed,
+    mx_pins.test_unit_scales_equal_plain_fp8,
+    lambda m: mx_pins.test_fraction_bruteforce(m, 0),
+    mx_pins.test_integer_valued_against_torch_matmul,
+    mx_pins.test_block_boundaries,
+    mx_pins.test_nan_scale_poisons_its_row_only,
+    mx_pins.test_strided_equals_packed,
 ]
 
 
