@@ -25,7 +25,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}
 PEAK_HBM_GBS = 8000.0
 
 
@@ -104,8 +104,12 @@ def cpu_baseline(w, x, seconds: float):
 
     def run(rows):
         t0 = time.perf_counter()
-        oracle.gemm(dt, A[:rows].ravel(), B.ravel(), rows, w.N, w.K,
-                    scale_a=x["scale_a"], scale_b=x["scale_b"], threads=threads, want_s=False)
+        if w.dtype == "mxfp8":
+            oracle.gemm_mx(A[:rows].ravel(), B.ravel(), x["SA"][:rows].numpy().ravel(),
+                           x["SB"].numpy().ravel(), rows, w.N, w.K, threads=threads, want_s=False)
+        else:
+            oracle.gemm(dt, A[:rows].ravel(), B.ravel(), rows, w.N, w.K,
+                        scale_a=x["scale_a"], scale_b=x["scale_b"], threads=threads, want_s=False)
         return time.perf_counter() - t0
 
     rows = max(1, threads // 2)
@@ -153,17 +157,29 @@ def main():
     A = x["A"].to(dev)
     B = x["B"].to(dev)
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
-    dtype_code = hk.HK_DTYPE_BF16 if w.dtype == "bf16" else hk.HK_DTYPE_FP8_E4M3
+    dtype_code = {"bf16": hk.HK_DTYPE_BF16, "fp8": hk.HK_DTYPE_FP8_E4M3,
+                  "mxfp8": hk.HK_DTYPE_MXFP8_E4M3}[w.dtype]
     opts = dict(schedule=a.schedule, grid_order=a.grid_order, group_m=a.group_m, window=a.window)
     plan = hk.hk_gemm_plan(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, **opts)
     stream = torch.cuda.Stream()
     sa, sb = x["scale_a"], x["scale_b"]
     inputs = {"A_sha256": gemm_inputs.sha256(x["A"]), "B_sha256": gemm_inputs.sha256(x["B"]),
               "scale_a": sa, "scale_b": sb}
+    if w.dtype == "mxfp8":
+        nb = (w.K + 31) // 32
+        SA = x["SA"].to(dev)
+        SB = x["SB"].to(dev)
+        inputs.update(SA_sha256=gemm_inputs.sha256(x["SA"]), SB_sha256=gemm_inputs.sha256(x["SB"]))
+        if a.schedule not in ("auto", "interleave4") or a.grid_order != "auto" or a.group_m or a.window:
+            print("MXFP8 runs the default 4-wave kernel and order only", file=sys.stderr)
+            sys.exit(2)
 
-    def step():
-        hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, sa, sb,
-                      stream=stream, **opts)
+        def step():
+            hk.hk_gemm_mxfp8(A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, SA, SB, nb, nb, stream=stream)
+    else:
+        def step():
+            hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, sa, sb,
+                          stream=stream, **opts)
 
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):

@@ -23,6 +23,7 @@ HK_ERROR_LAUNCH = 3
 
 HK_DTYPE_BF16 = 0
 HK_DTYPE_FP8_E4M3 = 1
+HK_DTYPE_MXFP8_E4M3 = 2
 
 HK_SCHEDULE_AUTO = 0
 HK_SCHEDULE_PINGPONG8 = 1
@@ -39,8 +40,8 @@ SCHEDULES = {"auto": 0, "pingpong8": 1, "interleave4": 2, "basic": 3, "interleav
              "smalltile": 5}
 GRID_ORDERS = {"auto": 0, "row_major": 1, "xcd": 2}
 
-EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_ex", "hk_gemm_plan", "hk_grid_map",
-            "hk_status_string", "hk_version")
+EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
+            "hk_grid_map", "hk_status_string", "hk_version")
 
 
 class HKError(RuntimeError):
@@ -85,6 +86,7 @@ def lib():
     i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     L.hk_gemm_bf16.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
     L.hk_gemm_fp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, vp]
+    L.hk_gemm_mxfp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, i64, vp]
     L.hk_gemm_ex.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
                              ctypes.POINTER(GemmOpts), vp]
     L.hk_gemm_plan.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64,
@@ -93,8 +95,8 @@ def lib():
     L.hk_status_string.argtypes = [i32]
     L.hk_status_string.restype = ctypes.c_char_p
     L.hk_version.argtypes = []
-    for name in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_ex", "hk_gemm_plan", "hk_grid_map",
-                 "hk_version"):
+    for name in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
+                 "hk_grid_map", "hk_version"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -147,6 +149,14 @@ def hk_gemm_fp8(A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b, stream=None,
     st = lib().hk_gemm_fp8(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                            float(scale_a), float(scale_b), _stream(stream))
     return _check(st, "hk_gemm_fp8", raise_on_error)
+
+
+def hk_gemm_mxfp8(A, B, C, M, N, K, lda, ldb, ldc, scales_a, scales_b, ld_scales_a,
+                  ld_scales_b, stream=None, raise_on_error=True):
+    """MXFP8: E4M3 A and B with E8M0 scale bytes, one per 32 K-elements of a row."""
+    st = lib().hk_gemm_mxfp8(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc, _ptr(scales_a),
+                             _ptr(scales_b), ld_scales_a, ld_scales_b, _stream(stream))
+    return _check(st, "hk_gemm_mxfp8", raise_on_error)
 
 
 def hk_gemm_ex(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,

@@ -114,6 +114,20 @@ __device__ __forceinline__ void mfma_fp8_16x16x128_pinned(f32x4& acc, i32x8 a, i
                  : "v"(a), "v"(b), "v"(one));
 }
 
+// 16x16x128 E4M3 with per-lane E8M0 block scales (byte 0 of sa for the "A"
+// operand, of sb for "B"), accumulator pinned to the AGPRs.  Lane l's scale
+// multiplies the 32 K-values of row l%16 in block l/16 of the instruction's
+// 128: K 32g..32g+31 of the operand layout above, where lane group g holds
+// K 16g..16g+15 in registers 0-3 and K 64+16g..64+16g+15 in registers 4-7
+// (so block g's 32 values sit in lane groups 2(g%2) and 2(g%2)+1, register
+// half g/2).  Measured on gfx950 with single-instruction probes.
+__device__ __forceinline__ void mfma_mxfp8_16x16x128_pinned(f32x4& acc, i32x8 a, i32x8 b,
+                                                            uint32_t sa, uint32_t sb) {
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b), "v"(sa), "v"(sb));
+}
+
 // Wait states that cover a matrix-core result (or an accumulator written by
 // ordinary instructions) before its next reader: 4 x 8 idle cycles, more
 // than the longest dependency the instructions above need.

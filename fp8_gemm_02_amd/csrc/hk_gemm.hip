@@ -53,7 +53,15 @@ hk_gemm_il4_bf16(hk::GemmArgs g) {
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
 hk_gemm_il4_fp8(hk::GemmArgs g) {
     HK_IL4_LDS;
-    hk::il4_fp8_body(g, buf0, buf1);
+    hk::il4_fp8_body<false>(g, buf0, buf1, nullptr);
+}
+
+// MXFP8: the FP8 4-wave kernel plus two 8 KiB buffers of block scales (144 KiB).
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_mxfp8(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    __shared__ hk::i32x4 scl[2 * hk::kMxGroupBytes / 16];
+    hk::il4_fp8_body<true>(g, buf0, buf1, (HK_LDS uint8_t*)scl);
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kI8Threads)
@@ -137,7 +145,8 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, int64_t M,
                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                    const hk_gemm_opts* opts) {
-    if (dtype != HK_DTYPE_BF16 && dtype != HK_DTYPE_FP8_E4M3) return HK_ERROR_INVALID_VALUE;
+    if (dtype != HK_DTYPE_BF16 && dtype != HK_DTYPE_FP8_E4M3 && dtype != HK_DTYPE_MXFP8_E4M3)
+        return HK_ERROR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return HK_ERROR_INVALID_VALUE;
     if (opts) {
         if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_SMALLTILE)
@@ -178,6 +187,13 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     const bool fast_ok = aligned(A, 16) && aligned(B, 16) && K % chunk == 0 &&
                          lda % chunk == 0 && ldb % chunk == 0 &&
                          lda_b * hk::kPP8Tile < kMaxRowBytes && ldb_b * hk::kPP8Tile < kMaxRowBytes;
+    if (dtype == HK_DTYPE_MXFP8_E4M3) {
+        // block scales: only the 4-wave kernel carries them, on the fast path
+        if (sched != HK_SCHEDULE_AUTO && sched != HK_SCHEDULE_INTERLEAVE4)
+            return HK_ERROR_NOT_SUPPORTED;
+        if (!fast_ok || K % 32 != 0) return HK_ERROR_NOT_SUPPORTED;
+        sched = HK_SCHEDULE_INTERLEAVE4;
+    }
     // Measured on MI355X: the 4-wave interleave is the faster kernel for both
     // dtypes at 8192^3; outputs with few 256 x 256 tiles (at most one per
     // four compute units) run faster on 128 x 128 tiles with more stages in
@@ -191,7 +207,8 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     if (sched != HK_SCHEDULE_BASIC && !fast_ok) return HK_ERROR_NOT_SUPPORTED;
     if (sched == HK_SCHEDULE_INTERLEAVE8 && dtype != HK_DTYPE_BF16) return HK_ERROR_NOT_SUPPORTED;
 
-    const bool fp8 = dtype == HK_DTYPE_FP8_E4M3;
+    const bool fp8 = dtype != HK_DTYPE_BF16;
+    const bool mx = dtype == HK_DTYPE_MXFP8_E4M3;
     if (sched == HK_SCHEDULE_PINGPONG8) {
         p->tile = hk::kPP8Tile;
         p->threads = hk::kPP8Threads;
@@ -214,8 +231,10 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
         p->tile = hk::kIL4Tile;
         p->threads = hk::kIL4Threads;
         p->lds_bytes = 4 * hk::kIL4StageI4 * 16;
-        p->kernel = fp8 ? (const void*)hk_gemm_il4_fp8 : (const void*)hk_gemm_il4_bf16;
-        p->name = fp8 ? "hk_gemm_il4_fp8" : "hk_gemm_il4_bf16";
+        p->kernel = mx ? (const void*)hk_gemm_il4_mxfp8
+                       : fp8 ? (const void*)hk_gemm_il4_fp8 : (const void*)hk_gemm_il4_bf16;
+        p->name = mx ? "hk_gemm_il4_mxfp8" : fp8 ? "hk_gemm_il4_fp8" : "hk_gemm_il4_bf16";
+        if (mx) p->lds_bytes += 2 * (int64_t)hk::kMxGroupBytes;
     } else {
         p->tile = hk::kBasicTile;
         p->threads = hk::kBasicThreads;
@@ -243,7 +262,10 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     g.lda_b = (uint32_t)lda_b;
     g.ldb_b = (uint32_t)ldb_b;
     g.ldc = ldc;
-    g.scale = fp8 ? scale : 1.0f;
+    g.scale = (fp8 && !mx) ? scale : 1.0f;
+    g.SA = nullptr;
+    g.SB = nullptr;
+    g.ldsa = g.ldsb = 0;
     g.c_align = (aligned(C, 8) && ldc % 4 == 0) ? 8 : (aligned(C, 4) && ldc % 2 == 0) ? 4 : 2;
     g.grid.order = order == HK_GRID_ROW_MAJOR ? hk::kGridRowMajor : hk::kGridXcd;
     g.grid.tiles_m = (int32_t)p->tiles_m;
@@ -273,9 +295,21 @@ hk_status launch(const Plan& p, hipStream_t stream) {
     return HK_SUCCESS;
 }
 
+hk_status zero_c(void* C, int64_t M, int64_t N, int64_t ldc, hipStream_t stream) {
+    const int64_t total = M * N;
+    const int64_t blocks = (total + 255) / 256;
+    if (blocks > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
+    hipLaunchKernelGGL(hk_zero_c, dim3((uint32_t)blocks), dim3(256), 0, stream, (uint16_t*)C, M,
+                       N, ldc);
+    if (hipGetLastError() != hipSuccess) return HK_ERROR_LAUNCH;
+    return HK_SUCCESS;
+}
+
 hk_status gemm_common(int32_t dtype, const void* A, const void* B, void* C, int64_t M, int64_t N,
                       int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale_a,
                       float scale_b, const hk_gemm_opts* opts, hipStream_t stream) {
+    // block-scaled FP8 needs its scale arrays: hk_gemm_mxfp8
+    if (dtype == HK_DTYPE_MXFP8_E4M3) return HK_ERROR_INVALID_VALUE;
     hk_status s = validate(dtype, A, B, C, M, N, K, lda, ldb, ldc, opts);
     if (s != HK_SUCCESS) return s;
     if (dtype == HK_DTYPE_FP8_E4M3 && (!isfinite(scale_a) || !isfinite(scale_b)))
@@ -284,15 +318,32 @@ hk_status gemm_common(int32_t dtype, const void* A, const void* B, void* C, int6
     Plan p;
     s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a * scale_b, opts, &p);
     if (s != HK_SUCCESS) return s;
-    if (K == 0) {
-        const int64_t total = M * N;
-        const int64_t blocks = (total + 255) / 256;
-        if (blocks > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
-        hipLaunchKernelGGL(hk_zero_c, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                           (uint16_t*)C, M, N, ldc);
-        if (hipGetLastError() != hipSuccess) return HK_ERROR_LAUNCH;
-        return HK_SUCCESS;
+    if (K == 0) return zero_c(C, M, N, ldc, stream);
+    return launch(p, stream);
+}
+
+hk_status gemm_mx(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int64_t ldc, const void* SA, const void* SB,
+                  int64_t ldsa, int64_t ldsb, hipStream_t stream) {
+    hk_status s = validate(HK_DTYPE_MXFP8_E4M3, A, B, C, M, N, K, lda, ldb, ldc, nullptr);
+    if (s != HK_SUCCESS) return s;
+    if (M == 0 || N == 0) return HK_SUCCESS;
+    if (K > 0) {
+        const int64_t nb = (K + 31) / 32;
+        if (SA == nullptr || SB == nullptr || ldsa < nb || ldsb < nb) return HK_ERROR_INVALID_VALUE;
+        // scales travel as 16-byte direct loads of whole rows
+        if (!aligned(SA, 16) || !aligned(SB, 16) || ldsa % 16 != 0 || ldsb % 16 != 0 ||
+            ldsa * hk::kIL4Tile >= kMaxRowBytes || ldsb * hk::kIL4Tile >= kMaxRowBytes)
+            return HK_ERROR_NOT_SUPPORTED;
     }
+    Plan p;
+    s = make_plan(HK_DTYPE_MXFP8_E4M3, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, nullptr, &p);
+    if (s != HK_SUCCESS) return s;
+    if (K == 0) return zero_c(C, M, N, ldc, stream);
+    p.args.SA = (const uint8_t*)SA;
+    p.args.SB = (const uint8_t*)SB;
+    p.args.ldsa = (uint32_t)ldsa;
+    p.args.ldsb = (uint32_t)ldsb;
     return launch(p, stream);
 }
 
@@ -313,6 +364,14 @@ hk_status hk_gemm_fp8(const void* A, const void* B, void* C, int64_t M, int64_t 
                       hk_stream_t stream) {
     return gemm_common(HK_DTYPE_FP8_E4M3, A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b,
                        nullptr, (hipStream_t)stream);
+}
+
+hk_status hk_gemm_mxfp8(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc, const void* scales_a,
+                        const void* scales_b, int64_t ld_scales_a, int64_t ld_scales_b,
+                        hk_stream_t stream) {
+    return gemm_mx(A, B, C, M, N, K, lda, ldb, ldc, scales_a, scales_b, ld_scales_a, ld_scales_b,
+                   (hipStream_t)stream);
 }
 
 hk_status hk_gemm_ex(int32_t dtype, const void* A, const void* B, void* C, int64_t M, int64_t N,

@@ -45,6 +45,10 @@ struct GemmArgs {
     float scale;            // multiplies the fp32 accumulator (FP8 only)
     int32_t c_align;        // guaranteed alignment of 4-column groups of C: 8, 4 or 2
     GridParams grid;
+    // MXFP8 only: E8M0 scale bytes, one per 32 K-elements of a row
+    const uint8_t* SA;
+    const uint8_t* SB;
+    uint32_t ldsa, ldsb;    // row strides of the scale arrays in bytes
 };
 
 constexpr int kRowBytes = 128;  // bytes of K per stage in every tile row
@@ -554,8 +558,24 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
 // The barrier is the only one per stage, with the same meaning as in the
 // BF16 form.  A(t, 2) and A(t, 3) are read in slice 0 itself, 16 and 24
 // MFMAs ahead of their first use.
+//
+// kMx: MXFP8, one E8M0 scale per 32 K-values of a row (OCP MX v1.0) in place
+// of the per-tensor scales.  A stage's 128 K are 4 scale blocks, and the
+// fragment layout above already gives lane group g block g's values of its
+// row, so lane l's scale operand for a block is byte 4s + l/16 of the row's
+// scales (stage s).  Scales travel HBM -> LDS in groups of four stages (16
+// bytes per row: 4 KiB per operand per group, one direct load of 64 rows
+// per wave and operand), issued with the loads of the group's first stage,
+// into two group buffers used in turn across tiles.  Each fragment's scale
+// is read (ds_read_u8) next to the fragment.  Blocks at or past K / 32 (the
+// zero-filled stages at the end of K) get scale 127 (x1), whatever the
+// bytes past a row's end hold.
+constexpr int kMxGroupStages = 4;
+constexpr uint32_t kMxGroupBytes = 2u * kIL4Tile * 16u;  // A and B scales of a group
+
+template <bool kMx>
 __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf0,
-                                             const IL4Buf buf1) {
+                                             const IL4Buf buf1, HK_LDS uint8_t* scl) {
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
@@ -579,6 +599,7 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     }
     struct Tile {
         i32x4 ra, rb;
+        i32x4 rsa, rsb;  // MXFP8: the tile's scale rows
         int32_t m0, n0;
     };
     auto tile = [&](uint32_t w) {
@@ -593,7 +614,44 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
                                (uint32_t)(sa > kOobOffset ? kOobOffset : sa));
         t.rb = make_rsrc_words(g.B + (int64_t)t.n0 * g.ldb_b,
                                (uint32_t)(sb > kOobOffset ? kOobOffset : sb));
+        if constexpr (kMx) {
+            const uint64_t xa = w < total ? (uint64_t)(g.M - t.m0) * g.ldsa : 0;
+            const uint64_t xb = w < total ? (uint64_t)(g.N - t.n0) * g.ldsb : 0;
+            t.rsa = make_rsrc_words(g.SA + (int64_t)t.m0 * g.ldsa,
+                                    (uint32_t)(xa > kOobOffset ? kOobOffset : xa));
+            t.rsb = make_rsrc_words(g.SB + (int64_t)t.n0 * g.ldsb,
+                                    (uint32_t)(xb > kOobOffset ? kOobOffset : xb));
+        }
         return t;
+    };
+    // ---- MXFP8 scales.  Group q of a tile (stages 4q .. 4q+3) lives in group
+    // buffer (seq + q) & 1, where seq counts the groups of earlier tiles.
+    // Buffer layout: A scales of the tile's 256 rows (16 bytes each: stage-in-
+    // group major, block minor), then B's.  Wave w loads rows 64w .. 64w+63.
+    const uint32_t nblocks = (uint32_t)g.K / 32u;
+    const uint32_t ngroups = (nk_pad + kMxGroupStages - 1) / kMxGroupStages;
+    auto send_scales = [&](const Tile& tt, uint32_t s, uint32_t seq) {
+        if constexpr (kMx) {
+            if (s % kMxGroupStages == 0) {
+                HK_LDS uint8_t* d = scl + (seq & 1u) * kMxGroupBytes + wave * 64u * 16u;
+                const uint32_t koff = (s / kMxGroupStages) * 16u;
+                load_lds_b128(tt.rsa, (HK_LDS void*)d, (wave * 64u + lane) * g.ldsa, koff);
+                load_lds_b128(tt.rsb, (HK_LDS void*)(d + kIL4Tile * 16u),
+                              (wave * 64u + lane) * g.ldsb, koff);
+            }
+        }
+    };
+    // scale byte of lane (row r16 of a 16-row block at tile row `row0`, block
+    // g4) for stage s of the tile whose group sequence starts at seq
+    auto rd_scale = [&](auto masked, uint32_t operand, uint32_t row0, uint32_t s,
+                        uint32_t seq) -> uint32_t {
+        const HK_LDS uint8_t* p = scl + ((seq + s / kMxGroupStages) & 1u) * kMxGroupBytes +
+                                  operand * (kIL4Tile * 16u) +
+                                  (row0 + (lane & 15u)) * 16u + (s % kMxGroupStages) * 4u +
+                                  (lane >> 4);
+        uint32_t v = *p;
+        if constexpr (decltype(masked)::value) v = 4u * s + (lane >> 4) < nblocks ? v : 127u;
+        return v;
     };
     auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s, int i) {
         const uint32_t koff = s * (uint32_t)kRowBytes;
@@ -624,6 +682,8 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     };
 
     f32x4 acc[8][8];
+    uint32_t xa[8], xb[8];  // MXFP8: scale operands of the fragments in fa, fb
+    uint32_t seq = 0;       // group sequence number of the current tile's group 0
     auto zero_acc = [&]() {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -635,54 +695,74 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     const uint32_t one = 127u;
     i32x8 fa[8], fb[8];
     // C^T block (mb, nb): B block nb as the "A" operand, A block mb as "B"
-    auto mfma = [&](int mb, int nb) { mfma_fp8_16x16x128_pinned(acc[mb][nb], fb[nb], fa[mb], one); };
+    auto mfma = [&](int mb, int nb) {
+        if constexpr (kMx)
+            mfma_mxfp8_16x16x128_pinned(acc[mb][nb], fb[nb], fa[mb], xb[nb], xa[mb]);
+        else
+            mfma_fp8_16x16x128_pinned(acc[mb][nb], fb[nb], fa[mb], one);
+    };
+    // fragment reads with their scales: stage s of the tile whose groups start
+    // at sequence number sq
+    auto get_a = [&](auto masked, const IL4Buf& d, int mb, uint32_t s, uint32_t sq) {
+        fa[mb] = rd_a(d, mb);
+        if constexpr (kMx) xa[mb] = rd_scale(masked, 0u, arow + 16u * (uint32_t)mb, s, sq);
+    };
+    auto get_b = [&](auto masked, const IL4Buf& d, int nb, uint32_t s, uint32_t sq) {
+        fb[nb] = rd_b(d, nb);
+        if constexpr (kMx) xb[nb] = rd_scale(masked, 1u, brow + 16u * (uint32_t)nb, s, sq);
+    };
 
     // slice 0 of stage t (in cur)
-    auto slice0 = [&](const IL4Buf& cur) {
+    auto slice0 = [&](auto masked, const IL4Buf& cur, uint32_t t) {
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
             mfma(q >> 3, q & 7);
-            if (q % 3 == 0 && q / 3 < 6) fa[2 + q / 3] = rd_a(cur, 2 + q / 3);
+            if (q % 3 == 0 && q / 3 < 6) get_a(masked, cur, 2 + q / 3, t, seq);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // slice 1 of stage t (in cur; stage t+1 in nxt), loading stage s of tile tt
-    auto slice1 = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
-                      const IL4Buf& nxt) {
+    // slice 1 of stage t (in cur; stage t+1 in nxt, stage u1 of the tile whose
+    // groups start at sequence sq1), loading stage s of tile tt (groups from ss)
+    auto slice1 = [&](auto masked, const Tile& tt, uint32_t s, uint32_t ss, const IL4Buf& cur,
+                      const IL4Buf& nxt, uint32_t u1, uint32_t sq1) {
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
             mfma(4 + (q & 3), q >> 2);
             if (q & 1) send(masked, tt, cur, s, q >> 1);
-            else if ((q & 3) == 0 && q > 0) fb[(q >> 2) - 1] = rd_b(nxt, (q >> 2) - 1);
-            else if (q == 2) fa[0] = rd_a(nxt, 0);
-            else if (q == 6) fa[1] = rd_a(nxt, 1);
+            else if ((q & 3) == 0 && q > 0) get_b(masked, nxt, (q >> 2) - 1, u1, sq1);
+            else if (q == 2) get_a(masked, nxt, 0, u1, sq1);
+            else if (q == 6) get_a(masked, nxt, 1, u1, sq1);
+            else if (q == 10) send_scales(tt, s, ss + s / kMxGroupStages);
             __builtin_amdgcn_sched_barrier(0);
         }
-        fb[7] = rd_b(nxt, 7);
+        get_b(masked, nxt, 7, u1, sq1);
     };
-    auto stage = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
-                     const IL4Buf& nxt) {
-        slice0(cur);
+    // stage t of the current tile; stage t+1 is stage u1 of the tile with group
+    // sequence sq1 (this tile, or the next one past the end of K)
+    auto stage = [&](auto masked, uint32_t t, const Tile& tt, uint32_t s, uint32_t ss,
+                     const IL4Buf& cur, const IL4Buf& nxt, uint32_t u1, uint32_t sq1) {
+        slice0(masked, cur, t);
         wait_lgkmcnt0();  // A(t, 2-7) are in registers: this wave is done with stage t
         wait_vmcnt0();    // this wave's share of stage t+1 has landed
         fenced_barrier();
-        slice1(masked, tt, s, cur, nxt);
+        slice1(masked, tt, s, ss, cur, nxt, u1, sq1);
     };
 
     const std::true_type masked;
     const std::false_type unmasked;
     uint32_t w = blockIdx.x;
     Tile cur = tile(w);
+    send_scales(cur, 0, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) send(masked, cur, buf0, 0, i);
 #pragma unroll
     for (int i = 0; i < 16; ++i) send(masked, cur, buf1, 1, i);
     wait_vmcnt<16>();
     fenced_barrier();
-    fa[0] = rd_a(buf0, 0);
-    fa[1] = rd_a(buf0, 1);
+    get_a(masked, buf0, 0, 0, 0);
+    get_a(masked, buf0, 1, 0, 0);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) fb[nb] = rd_b(buf0, nb);
+    for (int nb = 0; nb < 8; ++nb) get_b(masked, buf0, nb, 0, 0);
     zero_acc();
 
     for (;;) {
@@ -690,8 +770,8 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         const Tile nxt = tile(w_next);
         uint32_t t = 0;
         for (; t + 4 <= nk_whole; t += 2) {
-            stage(unmasked, cur, t + 2, buf0, buf1);
-            stage(unmasked, cur, t + 3, buf1, buf0);
+            stage(unmasked, t, cur, t + 2, seq, buf0, buf1, t + 1, seq);
+            stage(unmasked, t + 1, cur, t + 3, seq, buf1, buf0, t + 2, seq);
         }
         // stages at or past the end of this tile's K load the next tile's
         // first two (stage s of this tile is stage s - nk_pad of the next)
@@ -701,14 +781,24 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
             Tile r;
             r.ra = mine ? cur.ra : nxt.ra;
             r.rb = mine ? cur.rb : nxt.rb;
+            if constexpr (kMx) {
+                r.rsa = mine ? cur.rsa : nxt.rsa;
+                r.rsb = mine ? cur.rsb : nxt.rsb;
+            }
             return r;
         };
+        const uint32_t seq_next = seq + ngroups;
         for (; t < nk_pad; t += 2) {
             uint32_t s0, s1;
             const Tile t0 = pick(t + 2, &s0);
-            stage(masked, t0, s0, buf0, buf1);
+            const uint32_t q0 = t + 2 < nk_pad ? seq : seq_next;
+            stage(masked, t, t0, s0, q0, buf0, buf1, t + 1, seq);
             const Tile t1 = pick(t + 3, &s1);
-            stage(masked, t1, s1, buf1, buf0);
+            const uint32_t q1 = t + 3 < nk_pad ? seq : seq_next;
+            // stage t+2 is the next tile's stage 0 once t+2 reaches the end
+            const uint32_t u2 = t + 2 < nk_pad ? t + 2 : 0u;
+            const uint32_t qu = t + 2 < nk_pad ? seq : seq_next;
+            stage(masked, t + 1, t1, s1, q1, buf1, buf0, u2, qu);
         }
         acc_settle();  // the last MFMA results before the epilogue reads them
 
@@ -730,6 +820,7 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         if (w_next >= total) break;
         w = w_next;
         cur = nxt;
+        seq = seq_next;
         zero_acc();
     }
     wait_all();  // no LDS write may outlive the workgroup

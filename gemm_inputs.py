@@ -17,7 +17,14 @@ Workloads (M x N x K, operands K-contiguous, A is M x K, B is N x K):
 * ``bf16_mlp_ragged`` 8191 x 28670 x 8200, same distribution (odd M, N not a
                       multiple of the tile, K tail of 8);
 * ``fp8_8192``        8192^3, Normal(0, 1) scaled per tensor so that
-                      max |x| = 448, rounded to OCP e4m3, with fp32 scales.
+                      max |x| = 448, rounded to OCP e4m3, with fp32 scales;
+* ``mxfp8_8192``      8192^3, Normal(0, 1) quantised to MXFP8: per block of 32
+                      K-values of a row, shared scale 2^(floor(log2 amax) - 8)
+                      as an E8M0 byte, elements x / scale clamped to +-448 and
+                      rounded to e4m3 (the conversion of the OCP MX v1.0
+                      specification);
+* ``bf16_mlp_shard8`` 8192 x 3584 x 8192: one GPU's share of the MLP shape
+                      split eight ways along N.
 
 Seeds: workload index c gives A seed 1000c+1 and B seed 1000c+2; the integer
 variant adds 10.
@@ -39,7 +46,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str   # "bf16" or "fp8"
+    dtype: str   # "bf16", "fp8" or "mxfp8"
     dist: str    # "uniform", "normal", "normal002", "int4", "fp8_normal"
 
     @property
@@ -52,8 +59,9 @@ class Workload:
 
     @property
     def algorithmic_bytes(self) -> int:
-        """Read each input once, write C (bf16) once."""
-        return (self.M + self.N) * self.K * self.in_bytes + 2 * self.M * self.N
+        """Read each input once (with its block scales for MXFP8), write C (bf16) once."""
+        scales = (self.M + self.N) * ((self.K + 31) // 32) if self.dtype == "mxfp8" else 0
+        return (self.M + self.N) * self.K * self.in_bytes + scales + 2 * self.M * self.N
 
     def seeds(self, integer: bool = False):
         base = 1000 * self.index + (10 if integer else 0)
@@ -71,6 +79,7 @@ WORKLOADS = {
         # one GPU's share of the MLP shape split over 8 GPUs along N (448
         # tiles of 256 x 256: 1.75 windows of 256 co-resident workgroups)
         Workload("bf16_mlp_shard8", 3, 8192, 3584, 8192, "bf16", "normal002"),
+        Workload("mxfp8_8192", 5, 8192, 8192, 8192, "mxfp8", "mx_normal"),
     ]
 }
 
@@ -117,6 +126,36 @@ def fp8_matrix(rows: int, cols: int, seed: int, integer: bool = False):
     return q.view(torch.uint8), float(s)
 
 
+def mxfp8_matrix(rows: int, cols: int, seed: int, integer: bool = False):
+    """(e4m3 bytes (rows, cols), E8M0 scale bytes (rows, ceil(cols/32))) as uint8 CPU tensors.
+
+    Normal(0, 1) draws, quantised per block of 32 consecutive values of a row:
+    shared exponent e = floor(log2 amax) - 8 (8 = the exponent of e4m3's
+    largest normal, 448 = 1.75 * 2^8), scale byte e + 127 clamped to [0, 254],
+    elements x * 2^-e clamped to +-448 and rounded to e4m3 once.  An all-zero
+    block gets scale byte 127.  The integer variant draws elements in {-4..4}
+    and scale bytes in {126, 127, 128}, so that every sum of products is a
+    multiple of 1/4 below 2^21 for K up to 8192: exact in fp32.
+    """
+    g = _gen(seed)
+    nb = (cols + 31) // 32
+    if integer:
+        x = torch.randint(-4, 5, (rows, cols), generator=g).to(torch.float32)
+        sc = torch.randint(126, 129, (rows, nb), generator=g).to(torch.uint8)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8), sc
+    x = torch.randn(rows, cols, generator=g, dtype=torch.float32)
+    xp = torch.zeros(rows, nb * 32, dtype=torch.float32)
+    xp[:, :cols] = x
+    blocks = xp.view(rows, nb, 32)
+    amax = blocks.abs().amax(dim=2)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 8, torch.zeros_like(amax))
+    e = torch.clamp(e, -127, 127)
+    q = torch.clamp(blocks * torch.exp2(-e).unsqueeze(2), -E4M3_MAX, E4M3_MAX)
+    q = q.view(rows, nb * 32)[:, :cols].contiguous().to(torch.float8_e4m3fn)
+    sc = (e + 127).to(torch.uint8)
+    return q.view(torch.uint8), sc
+
+
 def make_inputs(w: Workload, integer: bool = False):
     """Return dict(A=..., B=..., scale_a=..., scale_b=...) as CPU tensors.
 
@@ -128,6 +167,10 @@ def make_inputs(w: Workload, integer: bool = False):
         A = bf16_matrix(w.M, w.K, dist, sa_seed)
         B = bf16_matrix(w.N, w.K, dist, sb_seed)
         return {"A": A, "B": B, "scale_a": 1.0, "scale_b": 1.0}
+    if w.dtype == "mxfp8":
+        A, SA = mxfp8_matrix(w.M, w.K, sa_seed, integer)
+        B, SB = mxfp8_matrix(w.N, w.K, sb_seed, integer)
+        return {"A": A, "B": B, "SA": SA, "SB": SB, "scale_a": 1.0, "scale_b": 1.0}
     A, sa = fp8_matrix(w.M, w.K, sa_seed, integer)
     B, sb = fp8_matrix(w.N, w.K, sb_seed, integer)
     return {"A": A, "B": B, "scale_a": sa, "scale_b": sb}

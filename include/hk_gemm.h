@@ -16,7 +16,8 @@
  * Element types.  BF16: 16-bit bfloat16 bit patterns.  FP8: OCP E4M3FN bytes
  * (bias 7, largest finite 448, S.1111.111 is NaN), one fp32 scale per tensor
  * passed by value.  The pages quote only an MXFP8 peak rate and no scaling
- * scheme; per-tensor scales are the plainest reading.  C is always bf16,
+ * scheme; per-tensor scales are the plainest reading.  Block-scaled MXFP8 has
+ * an entry point of its own (hk_gemm_mxfp8, below).  C is always bf16,
  * rounded to nearest even from the fp32 accumulator (times s for FP8).
  *
  * Ownership and ordering.  All pointers are device pointers owned by the
@@ -57,7 +58,8 @@ typedef enum hk_status {
 
 typedef enum hk_dtype {
     HK_DTYPE_BF16 = 0,
-    HK_DTYPE_FP8_E4M3 = 1
+    HK_DTYPE_FP8_E4M3 = 1,
+    HK_DTYPE_MXFP8_E4M3 = 2  /* block-scaled FP8: hk_gemm_mxfp8 (hk_gemm_plan describes it) */
 } hk_dtype;
 
 /*
@@ -142,8 +144,34 @@ hk_status hk_gemm_fp8(const void *A, const void *B, void *C,
                       float scale_a, float scale_b,
                       hk_stream_t stream);
 
-/* Either dtype with explicit options (opts may be NULL = defaults).
- * scale_a and scale_b are ignored for BF16. */
+/*
+ * MXFP8: E4M3FN elements with one E8M0 scale per 32 consecutive K-elements
+ * of a row (the block-scaled FP8 of the OCP Microscaling (MX) Formats
+ * specification v1.0, the format of the 5.0 PF FP8 peak quoted in "How to
+ * make AMD GPUs go brrr", section "AMD CDNA GPU structure"):
+ *
+ *     C[i*ldc + j] = bf16_rne( sum_{k<K} XA(i, k/32) A[i*lda + k] * XB(j, k/32) B[j*ldb + k] )
+ *
+ * with X(r, b) = 2^(x - 127) for the scale byte x = scales[r*ld_scales + b]
+ * (x = 255 is NaN).  scales_a holds M rows of ceil(K/32) bytes with row stride
+ * ld_scales_a, scales_b N rows with ld_scales_b (device pointers, caller-owned).
+ * Invalid (HK_ERROR_INVALID_VALUE): a NULL scale pointer or ld_scales below
+ * ceil(K/32) when K > 0, besides the checks of the other entry points.
+ * Not supported (HK_ERROR_NOT_SUPPORTED; no fallback kernel): K not a multiple
+ * of 32; A, B, scales_a or scales_b not 16-byte aligned; lda, ldb,
+ * ld_scales_a or ld_scales_b not a multiple of 16; 256 rows of any of them
+ * spanning 2^31 bytes or more.
+ */
+hk_status hk_gemm_mxfp8(const void *A, const void *B, void *C,
+                        int64_t M, int64_t N, int64_t K,
+                        int64_t lda, int64_t ldb, int64_t ldc,
+                        const void *scales_a, const void *scales_b,
+                        int64_t ld_scales_a, int64_t ld_scales_b,
+                        hk_stream_t stream);
+
+/* BF16 or FP8 with explicit options (opts may be NULL = defaults).
+ * scale_a and scale_b are ignored for BF16.  HK_DTYPE_MXFP8_E4M3 is
+ * HK_ERROR_INVALID_VALUE here (it needs hk_gemm_mxfp8's scale arrays). */
 hk_status hk_gemm_ex(int32_t dtype,
                      const void *A, const void *B, void *C,
                      int64_t M, int64_t N, int64_t K,

@@ -32,8 +32,8 @@ def L():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_ex", "hk_gemm_plan", "hk_grid_map",
-              "hk_status_string", "hk_version"):
+    for n in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
+              "hk_grid_map", "hk_status_string", "hk_version"):
         assert n in names
     assert set(names) == set(hk.EXPORTED)
 
@@ -89,6 +89,48 @@ def test_ex_rejects_bad_dtype_and_options(L):
     o.reserved[2] = 1
     st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0, ctypes.byref(o), None)
     assert st == hk.HK_ERROR_INVALID_VALUE
+
+
+def _mx(L, **kw):
+    a = dict(A=FAKE, B=FAKE, C=FAKE, M=32, N=32, K=256, lda=256, ldb=256, ldc=32, SA=FAKE,
+             SB=FAKE, ldsa=16, ldsb=16)
+    a.update(kw)
+    return L.hk_gemm_mxfp8(a["A"], a["B"], a["C"], a["M"], a["N"], a["K"], a["lda"], a["ldb"],
+                           a["ldc"], a["SA"], a["SB"], a["ldsa"], a["ldsb"], None)
+
+
+@pytest.mark.parametrize("bad", [dict(SA=0), dict(SB=0), dict(ldsa=7), dict(ldsb=0), dict(M=-1),
+                                 dict(A=0), dict(lda=255), dict(ldc=31)],
+                         ids=lambda b: ",".join(b))
+def test_mxfp8_invalid_arguments(L, bad):
+    assert _mx(L, **bad) == hk.HK_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("unsupported", [dict(K=48, lda=48, ldb=48, ldsa=16, ldsb=16),
+                                         dict(SA=FAKE + 8), dict(SB=FAKE + 4), dict(ldsa=24),
+                                         dict(ldsb=17), dict(A=FAKE + 16 + 8), dict(lda=264)],
+                         ids=lambda b: ",".join(b))
+def test_mxfp8_unsupported_layouts(L, unsupported):
+    assert _mx(L, **unsupported) == hk.HK_ERROR_NOT_SUPPORTED
+
+
+def test_mxfp8_needs_its_own_entry_point(L):
+    st = L.hk_gemm_ex(hk.HK_DTYPE_MXFP8_E4M3, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
+                      None, None)
+    assert st == hk.HK_ERROR_INVALID_VALUE
+    assert _mx(L, M=0) == hk.HK_SUCCESS and _mx(L, N=0, SA=0, SB=0) == hk.HK_SUCCESS
+
+
+def test_plan_mxfp8():
+    p = _plan(hk.HK_DTYPE_MXFP8_E4M3, 8192, 8192, 8192)
+    assert p["kernel_name"] == "hk_gemm_il4_mxfp8" and p["tile_k"] == 128
+    assert p["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4 and p["workgroups"] == 256
+    assert p["lds_bytes"] == 131072 + 16384  # two stages plus two groups of block scales
+    # small outputs run the same kernel (the only one that carries block scales)
+    p = _plan(hk.HK_DTYPE_MXFP8_E4M3, 256, 256, 256)
+    assert p["kernel_name"] == "hk_gemm_il4_mxfp8" and p["workgroups"] == 1
+    with pytest.raises(hk.HKError):
+        _plan(hk.HK_DTYPE_MXFP8_E4M3, 256, 256, 256, schedule="pingpong8")
 
 
 def test_empty_output_is_a_noop_success(L):
