@@ -138,3 +138,25 @@ def test_mxfp8_zero_k_and_empty():
     torch.cuda.synchronize()
     assert torch.all(C == 0)
     hk.hk_gemm_mxfp8(z, z, C, 0, 4, 32, 32, 32, 4, z, z, 16, 16)
+
+
+def test_mxfp8_nan_scale_matches_the_oracle():
+    """E8M0 255 is NaN (OCP MX): a block with that scale poisons its row of C
+    (scale of A) or its column (scale of B), on the GPU as in the oracle."""
+    M, N, K = 64, 64, 256
+    A, B, SA, SB = _inputs(M, N, K, 41, False)
+    SA = SA.clone()
+    SB = SB.clone()
+    SA[5, 3] = 255
+    SB[9, 0] = 255
+    SAp, SBp = _pad_cols(SA, 16, 127), _pad_cols(SB, 16, 127)
+    got = _run(A, B, SAp, SBp, M, N, K, K, K, 16, 16)
+    ref, S = oracle.gemm_mx(gemm_inputs.bits(A).ravel(), gemm_inputs.bits(B).ravel(),
+                            SAp.numpy().ravel(), SBp.numpy().ravel(), M, N, K, ldsa=16, ldsb=16)
+    gnan = np.isnan(oracle.bf16_to_f64(got))
+    rnan = np.isnan(oracle.bf16_to_f64(ref))
+    assert rnan.sum() == M + N - 1
+    assert np.array_equal(gnan, rnan)
+    st = oracle.compare(np.where(rnan, 0, got), np.where(rnan, 0, ref), np.where(rnan, 0, S),
+                        rel_tol=RTOL)
+    assert st["ok"], st
