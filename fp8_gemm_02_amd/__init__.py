@@ -31,13 +31,14 @@ HK_SCHEDULE_INTERLEAVE4 = 2
 HK_SCHEDULE_BASIC = 3
 HK_SCHEDULE_INTERLEAVE8 = 4
 HK_SCHEDULE_SMALLTILE = 5
+HK_SCHEDULE_PRODUCER_CONSUMER = 6
 
 HK_GRID_AUTO = 0
 HK_GRID_ROW_MAJOR = 1
 HK_GRID_XCD = 2
 
 SCHEDULES = {"auto": 0, "pingpong8": 1, "interleave4": 2, "basic": 3, "interleave8": 4,
-             "smalltile": 5}
+             "smalltile": 5, "producer_consumer": 6}
 GRID_ORDERS = {"auto": 0, "row_major": 1, "xcd": 2}
 
 EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",

@@ -82,6 +82,16 @@ hk_gemm_st4_fp8(hk::GemmArgs g) {
     hk::st4_body<true>(g, (HK_LDS hk::i32x4*)ring);
 }
 
+// Producer/consumer ablation: 4 loading waves, 4 computing waves, 256 x 128 tiles.
+extern "C" __global__ void __launch_bounds__(hk::kWSThreads)
+hk_gemm_ws_bf16(hk::GemmArgs g) {
+    __shared__ hk::i32x4 a0[hk::kWSStageAI4], b0[hk::kWSStageBI4], a1[hk::kWSStageAI4],
+        b1[hk::kWSStageBI4];
+    const hk::IL4Buf buf0 = {(HK_LDS hk::i32x4*)a0, (HK_LDS hk::i32x4*)b0};
+    const hk::IL4Buf buf1 = {(HK_LDS hk::i32x4*)a1, (HK_LDS hk::i32x4*)b1};
+    hk::ws_body(g, buf0, buf1);
+}
+
 extern "C" __global__ void __launch_bounds__(hk::kBasicThreads)
 hk_gemm_basic_bf16(hk::GemmArgs g) {
     __shared__ hk::i32x4 sA[hk::kBasicStageI4], sB[hk::kBasicStageI4];
@@ -130,7 +140,8 @@ struct Plan {
     int32_t dtype;
     int32_t schedule;
     int32_t grid_order;
-    int32_t tile;
+    int32_t tile;    // tile rows (M)
+    int32_t tile_n;  // tile columns (N); equal to tile unless set otherwise
     int32_t threads;
     int32_t lds_bytes;
     int64_t tiles_m, tiles_n;
@@ -149,7 +160,7 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
         return HK_ERROR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return HK_ERROR_INVALID_VALUE;
     if (opts) {
-        if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_SMALLTILE)
+        if (opts->schedule < HK_SCHEDULE_AUTO || opts->schedule > HK_SCHEDULE_PRODUCER_CONSUMER)
             return HK_ERROR_INVALID_VALUE;
         if (opts->grid_order < HK_GRID_AUTO || opts->grid_order > HK_GRID_XCD)
             return HK_ERROR_INVALID_VALUE;
@@ -171,6 +182,7 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
 hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, int64_t M,
                     int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale,
                     const hk_gemm_opts* opts, Plan* p) {
+    memset(p, 0, sizeof(*p));
     const int64_t esz = dtype == HK_DTYPE_BF16 ? 2 : 1;
     if (M > INT32_MAX - 512 || N > INT32_MAX - 512 || K > INT32_MAX / 2)
         return HK_ERROR_NOT_SUPPORTED;
@@ -205,7 +217,9 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
                          : (tiles256 * 4 <= cus ? HK_SCHEDULE_SMALLTILE : HK_SCHEDULE_INTERLEAVE4);
     }
     if (sched != HK_SCHEDULE_BASIC && !fast_ok) return HK_ERROR_NOT_SUPPORTED;
-    if (sched == HK_SCHEDULE_INTERLEAVE8 && dtype != HK_DTYPE_BF16) return HK_ERROR_NOT_SUPPORTED;
+    if ((sched == HK_SCHEDULE_INTERLEAVE8 || sched == HK_SCHEDULE_PRODUCER_CONSUMER) &&
+        dtype != HK_DTYPE_BF16)
+        return HK_ERROR_NOT_SUPPORTED;
 
     const bool fp8 = dtype != HK_DTYPE_BF16;
     const bool mx = dtype == HK_DTYPE_MXFP8_E4M3;
@@ -221,6 +235,13 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
         p->lds_bytes = 4 * hk::kIL4StageI4 * 16;
         p->kernel = (const void*)hk_gemm_i8_bf16;
         p->name = "hk_gemm_i8_bf16";
+    } else if (sched == HK_SCHEDULE_PRODUCER_CONSUMER) {
+        p->tile = hk::kWSTileM;
+        p->tile_n = hk::kWSTileN;
+        p->threads = hk::kWSThreads;
+        p->lds_bytes = 2 * (hk::kWSStageAI4 + hk::kWSStageBI4) * 16;
+        p->kernel = (const void*)hk_gemm_ws_bf16;
+        p->name = "hk_gemm_ws_bf16";
     } else if (sched == HK_SCHEDULE_SMALLTILE) {
         p->tile = hk::kSTTile;
         p->threads = hk::kSTThreads;
@@ -245,8 +266,9 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     p->dtype = dtype;
     p->schedule = sched;
     p->grid_order = order;
+    if (p->tile_n == 0) p->tile_n = p->tile;
     p->tiles_m = (M + p->tile - 1) / p->tile;
-    p->tiles_n = (N + p->tile - 1) / p->tile;
+    p->tiles_n = (N + p->tile_n - 1) / p->tile_n;
     if (p->tiles_m * p->tiles_n > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
 
     p->grid = p->tiles_m * p->tiles_n;
@@ -395,7 +417,7 @@ hk_status hk_gemm_plan(int32_t dtype, const void* A, const void* B, const void* 
     out->schedule = p.schedule;
     out->grid_order = p.grid_order;
     out->tile_m = p.tile;
-    out->tile_n = p.tile;
+    out->tile_n = p.tile_n;
     out->tile_k = hk::kRowBytes / (dtype == HK_DTYPE_BF16 ? 2 : 1);
     out->threads = p.threads;
     out->tiles_m = p.tiles_m;

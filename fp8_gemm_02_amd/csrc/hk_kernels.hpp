@@ -995,6 +995,173 @@ __device__ __forceinline__ void i8_body(const GemmArgs& g, const IL4Buf buf0, co
     }
 }
 
+// ----------------------------------------------- producer / consumer waves
+//
+// Wave specialisation, the alternative the pages measure their 8-wave
+// ping-pong against ("How to make AMD GPUs go brrr", section
+// "Intra-processor scheduling: wave patterns"): four producer waves issue
+// every HBM->LDS load, four consumer waves only read fragments and issue
+// MFMAs.  A SIMD's register file is split evenly between its waves, so a
+// consumer (sharing its SIMD with a producer) holds 128 accumulators: a
+// 128 x 64 sub-tile, which makes the workgroup tile 256 x 128.  BF16 only;
+// kept as the ablation of that design.
+//
+// LDS: two stage buffers of A (256 rows) and B (128 rows) x 128 bytes of K,
+// rows keyed row % 8 as in the other kernels.  One barrier per stage:
+//
+//   consumers:  slice 0 of stage t (MFMA on F(t,0) | read F(t,1)); wait for
+//               the reads; barrier; slice 1 (MFMA on F(t,1) | read F(t+1,0))
+//   producers:  wait for their loads of stage t+1; barrier; load stage t+2
+//               into the buffer the consumers just left
+constexpr int kWSThreads = 512;
+constexpr int kWSTileM = 256;
+constexpr int kWSTileN = 128;
+constexpr int kWSStageAI4 = kWSTileM * kChunks;
+constexpr int kWSStageBI4 = kWSTileN * kChunks;
+
+__device__ __forceinline__ void ws_body(const GemmArgs& g, const IL4Buf buf0, const IL4Buf buf1) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool producer = wave >= 4u;
+
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, g.grid, &tm, &tn);
+    const int32_t m0 = (int32_t)tm * kWSTileM;
+    const int32_t n0 = (int32_t)tn * kWSTileN;
+    const uint32_t kbytes = (uint32_t)g.K * 2u;
+    const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+    const uint32_t nk_pad = (nk + 1u) & ~1u;
+    const uint32_t nk_whole = kbytes / kRowBytes;
+    const std::true_type masked;
+    const std::false_type unmasked;
+
+    if (producer) {
+        // producer p sends A blocks p + 4j (j = 0..7) and B blocks p + 4j
+        // (j = 0..3): 12 loads per stage
+        const uint32_t p = wave - 4u;
+        const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
+        uint32_t span_a, span_b;
+        {
+            const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;  // rows past the edge read zero
+            const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
+            span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
+            span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
+        }
+        const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
+        const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
+        uint32_t voff_a[8], voff_b[4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            voff_a[j] = ((p + 4u * j) * 8u + (lane >> 3)) * g.lda_b + kc_lane * 16u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            voff_b[j] = ((p + 4u * j) * 8u + (lane >> 3)) * g.ldb_b + kc_lane * 16u;
+        auto issue = [&](auto msk, const IL4Buf& d, uint32_t s) {
+            const uint32_t koff = s * (uint32_t)kRowBytes;
+            const bool in_k = !decltype(msk)::value || koff + kc_lane * 16u < kbytes;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                load_lds_b128(rsrc_a, (HK_LDS void*)(d.a + (p + 4u * j) * 64u),
+                              in_k ? voff_a[j] : kOobOffset, koff);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                load_lds_b128(rsrc_b, (HK_LDS void*)(d.b + (p + 4u * j) * 64u),
+                              in_k ? voff_b[j] : kOobOffset, koff);
+        };
+        issue(masked, buf0, 0);
+        issue(masked, buf1, 1);
+        wait_vmcnt<12>();  // stage 0 landed
+        fenced_barrier();
+        for (uint32_t t = 0; t < nk_pad; t += 2) {
+            wait_vmcnt0();  // stage t+1 landed
+            fenced_barrier();
+            if (t + 2 < nk_pad) {
+                if (t + 2 < nk_whole) issue(unmasked, buf0, t + 2);
+                else issue(masked, buf0, t + 2);
+            }
+            wait_vmcnt0();
+            fenced_barrier();
+            if (t + 3 < nk_pad) {
+                if (t + 3 < nk_whole) issue(unmasked, buf1, t + 3);
+                else issue(masked, buf1, t + 3);
+            }
+        }
+        wait_all();  // no LDS write may outlive the workgroup
+        return;
+    }
+
+    // ---- consumers: wave c owns A rows (c / 2) * 128 .. +127 and B rows
+    // (c % 2) * 64 .. +63 as 8 x 4 blocks of 16 x 16
+    const uint32_t wm = wave >> 1;
+    const uint32_t wn = wave & 1u;
+    const uint32_t r16 = lane & 15u;
+    const uint32_t g4 = lane >> 4;
+    const uint32_t fo0 = r16 * kChunks + ((0u + g4) ^ (r16 & 7u));
+    const uint32_t fo1 = r16 * kChunks + ((4u + g4) ^ (r16 & 7u));
+    const uint32_t arow = wm * 128u;
+    const uint32_t brow = wn * 64u;
+    auto read = [&](const IL4Buf& d, int s, int f) -> i32x4 {
+        const HK_LDS i32x4* base = f < 8 ? d.a + (arow + 16u * (uint32_t)f) * kChunks
+                                         : d.b + (brow + 16u * (uint32_t)(f - 8)) * kChunks;
+        return base[s == 0 ? fo0 : fo1];
+    };
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x4 fx[12], fy[12];
+    auto mfma = [&](const i32x4 (&fr)[12], int q) {
+        const int mb = q >> 2, nb = q & 3;
+        acc[mb][nb] = mfma_bf16_16x16x32(fr[8 + nb], fr[mb], acc[mb][nb]);
+    };
+    // fragments in consumption order: A block 0, B blocks 0-3, A blocks 1-7
+    auto rd = [&](i32x4 (&fr)[12], const IL4Buf& d, int s, int r) {
+        constexpr int kOrder[12] = {0, 8, 9, 10, 11, 1, 2, 3, 4, 5, 6, 7};
+        fr[kOrder[r]] = read(d, s, kOrder[r]);
+    };
+    auto stage = [&](const IL4Buf& cur, const IL4Buf& nxt) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            mfma(fx, q);
+            if ((q & 1) && q < 24) rd(fy, cur, 1, q >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_lgkmcnt0();  // F(t, 1) is in registers: done with this stage's buffer
+        fenced_barrier();
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            mfma(fy, q);
+            if ((q & 1) && q < 24) rd(fx, nxt, 0, q >> 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        pin_all(acc);
+    };
+    fenced_barrier();  // stage 0 landed
+#pragma unroll
+    for (int r = 0; r < 12; ++r) rd(fx, buf0, 0, r);
+    for (uint32_t t = 0; t < nk_pad; t += 2) {
+        stage(buf0, buf1);
+        stage(buf1, buf0);
+    }
+    wait_all();
+
+    const int32_t mrow = m0 + (int32_t)(arow + r16);
+    const int32_t ncol = n0 + (int32_t)(brow + g4 * 4u);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int32_t m = mrow + mb * 16;
+        if (m < g.M) {
+            uint16_t* crow = g.C + (int64_t)m * g.ldc;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int32_t n = ncol + nb * 16;
+                if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb], g.c_align);
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------- small outputs
 //
 // For outputs with few 256 x 256 tiles, where the GEMM is bound by the

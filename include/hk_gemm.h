@@ -76,7 +76,10 @@ typedef enum hk_dtype {
  *   INTERLEAVE8 8 waves per CU, each interleaving its own loads with its
  *               matrix-core instructions (BF16 only);
  *   SMALLTILE   128 x 128 tiles with four K stages in flight, for outputs
- *               too small to give every CU a 256 x 256 tile.
+ *               too small to give every CU a 256 x 256 tile;
+ *   PRODUCER_CONSUMER  4 waves that only load and 4 that only compute, 256 x
+ *               128 tiles (BF16 only; the wave-specialised design the pages
+ *               compare the ping-pong against, kept as an ablation).
  * AUTO, when the fast-path conditions hold (16-byte aligned A and B, K, lda
  * and ldb whole 16-byte chunks), picks SMALLTILE if the output has at most
  * one 256 x 256 tile per four compute units and INTERLEAVE4 (the fastest on
@@ -88,7 +91,8 @@ typedef enum hk_schedule {
     HK_SCHEDULE_INTERLEAVE4 = 2,
     HK_SCHEDULE_BASIC = 3,
     HK_SCHEDULE_INTERLEAVE8 = 4,
-    HK_SCHEDULE_SMALLTILE = 5
+    HK_SCHEDULE_SMALLTILE = 5,
+    HK_SCHEDULE_PRODUCER_CONSUMER = 6
 } hk_schedule;
 
 /*

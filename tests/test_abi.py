@@ -267,6 +267,16 @@ def test_plan_explicit_schedules(schedule, dtype, name, threads):
     assert (p["tile_m"], p["tile_n"]) == (256, 256) and p["lds_bytes"] == 131072
 
 
+def test_plan_producer_consumer():
+    p = _plan(hk.HK_DTYPE_BF16, 8192, 8192, 8192, schedule="producer_consumer")
+    assert p["kernel_name"] == "hk_gemm_ws_bf16" and p["threads"] == 512
+    assert (p["tile_m"], p["tile_n"]) == (256, 128) and (p["tiles_m"], p["tiles_n"]) == (32, 64)
+    assert p["workgroups"] == 32 * 64 and p["lds_bytes"] == 2 * (256 + 128) * 128
+    with pytest.raises(hk.HKError) as e:
+        _plan(hk.HK_DTYPE_FP8_E4M3, 256, 256, 256, schedule="producer_consumer")
+    assert e.value.status == hk.HK_ERROR_NOT_SUPPORTED
+
+
 def test_interleave8_is_bf16_only():
     with pytest.raises(hk.HKError) as e:
         _plan(hk.HK_DTYPE_FP8_E4M3, 256, 256, 256, schedule="interleave8")

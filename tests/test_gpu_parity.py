@@ -110,10 +110,13 @@ def test_fp8_ragged_full(M, N, K, integer):
     _full_check("fp8", A, B, M, N, K, K, K, exact=integer, sa=sa, sb=sb)
 
 
-@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "smalltile", "basic"])
+@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "smalltile", "basic",
+                                      "interleave8", "producer_consumer"])
 @pytest.mark.parametrize("grid_order", ["row_major", "xcd"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_every_variant(schedule, grid_order, dtype):
+    if schedule in ("interleave8", "producer_consumer") and dtype == "fp8":
+        pytest.skip("BF16-only schedule")
     M, N, K = 777, 1029, 512
     if dtype == "bf16":
         A, B, sa, sb = _bf16(M, K, "normal", 11), _bf16(N, K, "normal", 12), 1.0, 1.0
@@ -124,13 +127,14 @@ def test_every_variant(schedule, grid_order, dtype):
                 grid_order=grid_order)
 
 
-@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "interleave8", "smalltile"])
+@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "interleave8", "smalltile",
+                                      "producer_consumer"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("M,N,K", [(513, 769, 1040), (256, 256, 128), (300, 40, 16)])
 def test_fast_schedules_ragged_integer(schedule, dtype, M, N, K):
     """Bit-exact on integer-valued inputs: edge tiles, K tails and odd stage counts."""
-    if schedule == "interleave8" and dtype == "fp8":
-        pytest.skip("the 8-wave interleave kernel is BF16 only")
+    if schedule in ("interleave8", "producer_consumer") and dtype == "fp8":
+        pytest.skip("BF16-only schedule")
     if dtype == "bf16":
         A, B, sa, sb = _bf16(M, K, "int4", M + 3), _bf16(N, K, "int4", N + 4), 1.0, 1.0
     else:
