@@ -154,15 +154,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = gemm_inputs.make_inputs(w)
-    A = x["A"].to(dev)
-    B = x["B"].to(dev)
+    A_st, B_st = gemm_inputs.stored(w, x)
+    A = A_st.to(dev)
+    B = B_st.to(dev)
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
     dtype_code = {"bf16": hk.HK_DTYPE_BF16, "fp8": hk.HK_DTYPE_FP8_E4M3,
                   "mxfp8": hk.HK_DTYPE_MXFP8_E4M3}[w.dtype]
-    opts = dict(schedule=a.schedule, grid_order=a.grid_order, group_m=a.group_m, window=a.window)
-    plan = hk.hk_gemm_plan(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, **opts)
+    opts = dict(schedule=a.schedule, grid_order=a.grid_order, group_m=a.group_m, window=a.window,
+                layout_a=w.layout_a, layout_b=w.layout_b)
+    plan = hk.hk_gemm_plan(dtype_code, A, B, C, w.M, w.N, w.K, w.lda, w.ldb, w.N, **opts)
     stream = torch.cuda.Stream()
     sa, sb = x["scale_a"], x["scale_b"]
+    # digests of the logical M x K and N x K matrices (the stored arrays are
+    # their transposes for a K-strided layout)
     inputs = {"A_sha256": gemm_inputs.sha256(x["A"]), "B_sha256": gemm_inputs.sha256(x["B"]),
               "scale_a": sa, "scale_b": sb}
     if w.dtype == "mxfp8":
@@ -178,7 +182,7 @@ def main():
             hk.hk_gemm_mxfp8(A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, SA, SB, nb, nb, stream=stream)
     else:
         def step():
-            hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, sa, sb,
+            hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.lda, w.ldb, w.N, sa, sb,
                           stream=stream, **opts)
 
     torch.cuda.synchronize()
@@ -222,7 +226,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
-                   "a_layout": "MxK row-major", "b_layout": "NxK row-major",
+                   "a_layout": "KxM row-major" if w.layout_a else "MxK row-major",
+                   "b_layout": "KxN row-major" if w.layout_b else "NxK row-major",
                    "distribution": w.dist, "kernel": plan["kernel_name"],
                    "schedule": plan["schedule"], "grid_order": plan["grid_order"],
                    "group_m": plan["group_m"], "window": plan["window"]},

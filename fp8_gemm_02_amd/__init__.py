@@ -37,9 +37,13 @@ HK_GRID_AUTO = 0
 HK_GRID_ROW_MAJOR = 1
 HK_GRID_XCD = 2
 
+HK_LAYOUT_K_CONTIGUOUS = 0  # A stored M x K, B stored N x K
+HK_LAYOUT_K_STRIDED = 1     # A stored K x M, B stored K x N
+
 SCHEDULES = {"auto": 0, "pingpong8": 1, "interleave4": 2, "basic": 3, "interleave8": 4,
              "smalltile": 5, "producer_consumer": 6}
 GRID_ORDERS = {"auto": 0, "row_major": 1, "xcd": 2}
+LAYOUTS = {"k_contiguous": 0, "k_strided": 1}
 
 EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
             "hk_grid_map", "hk_status_string", "hk_version")
@@ -54,7 +58,8 @@ class HKError(RuntimeError):
 class GemmOpts(ctypes.Structure):
     _fields_ = [("schedule", ctypes.c_int32), ("grid_order", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -124,13 +129,16 @@ def _stream(s) -> int:
     return int(s.cuda_stream)
 
 
-def _opts(schedule=0, grid_order=0, group_m=0, window=0):
+def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0):
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
     if isinstance(grid_order, str):
         grid_order = GRID_ORDERS[grid_order]
+    layout_a = LAYOUTS[layout_a] if isinstance(layout_a, str) else layout_a
+    layout_b = LAYOUTS[layout_b] if isinstance(layout_b, str) else layout_b
     o = GemmOpts()
     o.schedule, o.grid_order, o.group_m, o.window = schedule, grid_order, group_m, window
+    o.layout_a, o.layout_b = layout_a, layout_b
     return o
 
 
@@ -161,18 +169,18 @@ def hk_gemm_mxfp8(A, B, C, M, N, K, lda, ldb, ldc, scales_a, scales_b, ld_scales
 
 
 def hk_gemm_ex(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,
-               schedule=0, grid_order=0, group_m=0, window=0, stream=None,
-               raise_on_error=True):
-    o = _opts(schedule, grid_order, group_m, window)
+               schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
+               stream=None, raise_on_error=True):
+    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b)
     st = lib().hk_gemm_ex(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                           float(scale_a), float(scale_b), ctypes.byref(o), _stream(stream))
     return _check(st, "hk_gemm_ex", raise_on_error)
 
 
 def hk_gemm_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, schedule=0, grid_order=0,
-                 group_m=0, window=0):
+                 group_m=0, window=0, layout_a=0, layout_b=0):
     """Return the launch description as a dict; raises HKError on invalid input."""
-    o = _opts(schedule, grid_order, group_m, window)
+    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b)
     info = PlanInfo()
     st = lib().hk_gemm_plan(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                             ctypes.byref(o), ctypes.byref(info))
@@ -221,4 +229,42 @@ def gemm_nt(A, B, scale_a=None, scale_b=None, out=None, stream=None, **opts):
                B.stride(0) if N > 1 else max(K, 1), out.stride(0) if M > 1 else max(N, 1),
                1.0 if scale_a is None else scale_a, 1.0 if scale_b is None else scale_b,
                stream=stream, **opts)
+    return out
+
+
+def matmul(A, B, scale_a=None, scale_b=None, out=None, stream=None, **opts):
+    """C = A @ B for 2-D torch device tensors A (M x K) and B (K x N), bf16, or
+    uint8/float8_e4m3fn with scales, where each operand is contiguous along one
+    of its two dimensions (a plain tensor or a transposed view of one).
+
+    The storage decides the layout: A with unit stride along K is stored M x K
+    (K_CONTIGUOUS), along M it is stored K x M (K_STRIDED); B with unit stride
+    along K is an N x K array seen transposed (K_CONTIGUOUS), along N it is
+    stored K x N (K_STRIDED).  Allocates C (bf16) with torch when `out` is None.
+    """
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+
+    def layout(kstride, rstride, rows):
+        # (layout, leading dimension) from the strides along K and along rows
+        if kstride == 1 and (rows <= 1 or rstride >= K):
+            return HK_LAYOUT_K_CONTIGUOUS, rstride if rows > 1 else max(K, 1)
+        if rstride == 1 and (K <= 1 or kstride >= rows):
+            return HK_LAYOUT_K_STRIDED, kstride if K > 1 else max(rows, 1)
+        raise ValueError("each operand must be contiguous along one dimension")
+
+    la, lda = layout(A.stride(1), A.stride(0), M)
+    lb, ldb = layout(B.stride(0), B.stride(1), N)
+    fp8 = A.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if out.stride(1) != 1:
+        raise ValueError("C rows must be contiguous")
+    dtype = HK_DTYPE_FP8_E4M3 if fp8 else HK_DTYPE_BF16
+    hk_gemm_ex(dtype, A, B, out, M, N, K, lda, ldb, out.stride(0) if M > 1 else max(N, 1),
+               1.0 if scale_a is None else scale_a, 1.0 if scale_b is None else scale_b,
+               layout_a=la, layout_b=lb, stream=stream, **opts)
     return out

@@ -47,7 +47,26 @@ hk_gemm_pp8_fp8(hk::GemmArgs g) {
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
 hk_gemm_il4_bf16(hk::GemmArgs g) {
     HK_IL4_LDS;
-    hk::il4_bf16_body(g, buf0, buf1);
+    hk::il4_bf16_body<false, false>(g, buf0, buf1);
+}
+
+// operands stored K-strided: A as K x M ("akm"), B as K x N ("bkn")
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_bf16_akm(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_bf16_body<true, false>(g, buf0, buf1);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_bf16_bkn(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_bf16_body<false, true>(g, buf0, buf1);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_bf16_akm_bkn(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_bf16_body<true, true>(g, buf0, buf1);
 }
 
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
@@ -165,13 +184,19 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
         if (opts->grid_order < HK_GRID_AUTO || opts->grid_order > HK_GRID_XCD)
             return HK_ERROR_INVALID_VALUE;
         if (opts->group_m < 0 || opts->window < 0) return HK_ERROR_INVALID_VALUE;
-        for (int i = 0; i < 4; ++i)
+        for (int32_t l : {opts->layout_a, opts->layout_b})
+            if (l != HK_LAYOUT_K_CONTIGUOUS && l != HK_LAYOUT_K_STRIDED)
+                return HK_ERROR_INVALID_VALUE;
+        for (int i = 0; i < 2; ++i)
             if (opts->reserved[i] != 0) return HK_ERROR_INVALID_VALUE;
     }
     if (M == 0 || N == 0) return HK_SUCCESS;
     if (C == nullptr || ldc < N || !aligned(C, 2)) return HK_ERROR_INVALID_VALUE;
     if (K > 0) {
-        if (A == nullptr || B == nullptr || lda < K || ldb < K) return HK_ERROR_INVALID_VALUE;
+        const bool at = opts && opts->layout_a == HK_LAYOUT_K_STRIDED;
+        const bool bt = opts && opts->layout_b == HK_LAYOUT_K_STRIDED;
+        if (A == nullptr || B == nullptr || lda < (at ? M : K) || ldb < (bt ? N : K))
+            return HK_ERROR_INVALID_VALUE;
         if (dtype == HK_DTYPE_BF16 && (!aligned(A, 2) || !aligned(B, 2)))
             return HK_ERROR_INVALID_VALUE;
     }
@@ -194,11 +219,27 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     if (order == HK_GRID_AUTO) order = HK_GRID_XCD;
 
     // Fast path: 16-byte direct loads need 16-byte aligned rows and whole
-    // 16-byte K chunks; 256 rows of stride must fit the 31-bit offsets.
+    // 16-byte chunks; 256 rows of stride must fit the 31-bit offsets.  An
+    // operand stored K-strided is read in rows of K: its M (or N) must be
+    // whole chunks, and K + 128 rows (the stages past K included) must fit.
+    const bool at = opts && opts->layout_a == HK_LAYOUT_K_STRIDED;
+    const bool bt = opts && opts->layout_b == HK_LAYOUT_K_STRIDED;
     const int64_t chunk = 16 / esz;
-    const bool fast_ok = aligned(A, 16) && aligned(B, 16) && K % chunk == 0 &&
-                         lda % chunk == 0 && ldb % chunk == 0 &&
-                         lda_b * hk::kPP8Tile < kMaxRowBytes && ldb_b * hk::kPP8Tile < kMaxRowBytes;
+    auto operand_ok = [&](const void* X, bool trans, int64_t rows, int64_t ld, int64_t ld_b) {
+        if (!aligned(X, 16) || ld % chunk != 0) return false;
+        if (trans) return rows % chunk == 0 && (K + 128) * ld_b + 512 < kMaxRowBytes;
+        return K % chunk == 0 && ld_b * hk::kPP8Tile < kMaxRowBytes;
+    };
+    const bool fast_ok = operand_ok(A, at, M, lda, lda_b) && operand_ok(B, bt, N, ldb, ldb_b);
+    const bool trans = at || bt;
+    if (trans) {
+        // the 4-wave BF16 kernel reads K-strided images; BASIC reads anything
+        if (sched == HK_SCHEDULE_AUTO)
+            sched = fast_ok && dtype == HK_DTYPE_BF16 ? HK_SCHEDULE_INTERLEAVE4 : HK_SCHEDULE_BASIC;
+        if (sched != HK_SCHEDULE_BASIC &&
+            (sched != HK_SCHEDULE_INTERLEAVE4 || dtype != HK_DTYPE_BF16))
+            return HK_ERROR_NOT_SUPPORTED;
+    }
     if (dtype == HK_DTYPE_MXFP8_E4M3) {
         // block scales: only the 4-wave kernel carries them, on the fast path
         if (sched != HK_SCHEDULE_AUTO && sched != HK_SCHEDULE_INTERLEAVE4)
@@ -252,9 +293,25 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
         p->tile = hk::kIL4Tile;
         p->threads = hk::kIL4Threads;
         p->lds_bytes = 4 * hk::kIL4StageI4 * 16;
-        p->kernel = mx ? (const void*)hk_gemm_il4_mxfp8
-                       : fp8 ? (const void*)hk_gemm_il4_fp8 : (const void*)hk_gemm_il4_bf16;
-        p->name = mx ? "hk_gemm_il4_mxfp8" : fp8 ? "hk_gemm_il4_fp8" : "hk_gemm_il4_bf16";
+        if (mx) {
+            p->kernel = (const void*)hk_gemm_il4_mxfp8;
+            p->name = "hk_gemm_il4_mxfp8";
+        } else if (fp8) {
+            p->kernel = (const void*)hk_gemm_il4_fp8;
+            p->name = "hk_gemm_il4_fp8";
+        } else if (at && bt) {
+            p->kernel = (const void*)hk_gemm_il4_bf16_akm_bkn;
+            p->name = "hk_gemm_il4_bf16_akm_bkn";
+        } else if (at) {
+            p->kernel = (const void*)hk_gemm_il4_bf16_akm;
+            p->name = "hk_gemm_il4_bf16_akm";
+        } else if (bt) {
+            p->kernel = (const void*)hk_gemm_il4_bf16_bkn;
+            p->name = "hk_gemm_il4_bf16_bkn";
+        } else {
+            p->kernel = (const void*)hk_gemm_il4_bf16;
+            p->name = "hk_gemm_il4_bf16";
+        }
         if (mx) p->lds_bytes += 2 * (int64_t)hk::kMxGroupBytes;
     } else {
         p->tile = hk::kBasicTile;
@@ -288,6 +345,8 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     g.SA = nullptr;
     g.SB = nullptr;
     g.ldsa = g.ldsb = 0;
+    g.a_t = at;
+    g.b_t = bt;
     g.c_align = (aligned(C, 8) && ldc % 4 == 0) ? 8 : (aligned(C, 4) && ldc % 2 == 0) ? 4 : 2;
     g.grid.order = order == HK_GRID_ROW_MAJOR ? hk::kGridRowMajor : hk::kGridXcd;
     g.grid.tiles_m = (int32_t)p->tiles_m;

@@ -49,6 +49,9 @@ struct GemmArgs {
     const uint8_t* SA;
     const uint8_t* SB;
     uint32_t ldsa, ldsb;    // row strides of the scale arrays in bytes
+    // operand stored transposed: A[k * lda + m], B[k * ldb + n] (basic kernel;
+    // the 4-wave BF16 kernel takes the layout as template arguments)
+    int32_t a_t, b_t;
 };
 
 constexpr int kRowBytes = 128;  // bytes of K per stage in every tile row
@@ -339,6 +342,28 @@ struct IL4Buf {
 // The stage pipeline runs through tile boundaries: the two stages loaded
 // past a tile's last one are the next tile's first two, so between tiles
 // only the store of C remains.
+//
+// kAT, kBT: the operand is stored transposed (A as K x M, B as K x N: M or N
+// contiguous, row stride lda or ldb), so that C = A^T B^T, A^T B or A B as
+// well as A B^T.  A stage of such an operand is 64 K-rows x 512 bytes (the
+// tile's 256 rows of the other index), loaded with the same direct loads (one
+// load covers two K-rows; K-rows past K read zero through the buffer bounds)
+// into an image whose 16-byte chunk c of K-row k sits at c ^ km_key(k).  A
+// fragment (16 rows x 32 K) is built by two transposing reads
+// (ds_read_b64_tr_b16).  Within each group of 16 lanes, output lane i's
+// element r comes from source lane (i >> 2) + 4r, position i & 3 (measured
+// on gfx950).  So source lane (a + 4r) of lane group g addresses K-row
+// 8g + 4h + r, rows 4a .. 4a+3 of the block, and output lane i receives row
+// i, K 8g + 4h .. +3: half of the MFMA operand, exactly what a K-contiguous
+// image gives.  The key puts the 8 K-rows that one half-wave's read touches
+// on distinct 32-byte bank groups.
+__device__ __forceinline__ uint32_t km_key(uint32_t k) {
+    return ((k & 3u) | (((k >> 3) & 3u) << 2)) << 1;
+}
+constexpr uint32_t kKMRowBytes = kIL4Tile * 2u;    // one K-row of a transposed stage image
+constexpr uint32_t kKMStageRows = kRowBytes / 2u;  // 64 K-rows of bf16 per stage
+
+template <bool kAT, bool kBT>
 __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf buf0,
                                               const IL4Buf buf1) {
     const uint32_t lane = threadIdx.x & 63u;
@@ -355,12 +380,16 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     // chunk l%8 holding logical chunk (l%8) ^ (l/8).  Wave w sends blocks
     // w + 4j (j = 0..7) of A and of B: 16 loads per stage.
     const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
+    // Transposed operand: block wave + 4j = K-rows 2(wave + 4j), +1 of the
+    // stage; lane l -> K-row 2 * block + l/32, physical chunk l%32.
     uint32_t voff_a[8], voff_b[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t row = (wave + 4u * j) * 8u + (lane >> 3);
-        voff_a[j] = row * g.lda_b + kc_lane * 16u;
-        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
+        const uint32_t krow = 2u * (wave + 4u * j) + (lane >> 5);
+        const uint32_t kmo = ((lane & 31u) ^ km_key(krow)) * 16u;
+        voff_a[j] = kAT ? krow * g.lda_b + kmo : row * g.lda_b + kc_lane * 16u;
+        voff_b[j] = kBT ? krow * g.ldb_b + kmo : row * g.ldb_b + kc_lane * 16u;
     }
     // Buffer resources of tile w's A and B row panels; rows past the matrix
     // edge read as zero.  A tile past the end (w >= total) gets empty
@@ -369,18 +398,24 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         i32x4 ra, rb;
         int32_t m0, n0;
     };
+    // rows r0 .. of an operand with `rows` rows: K-contiguous, the panel ends
+    // with row rows - 1; transposed, it ends at K-row K - 1, row rows - 1
+    auto panel = [&](bool trans, const uint8_t* X, uint32_t ld_b, int32_t rows, int32_t r0,
+                     bool live) {
+        const uint64_t sz = !live   ? 0
+                            : trans ? (uint64_t)(g.K - 1) * ld_b + (uint64_t)(rows - r0) * 2u
+                                    : (uint64_t)(rows - r0) * ld_b;
+        const uint8_t* base = X + (trans ? (int64_t)r0 * 2 : (int64_t)r0 * ld_b);
+        return make_rsrc_words(base, (uint32_t)(sz > kOobOffset ? kOobOffset : sz));
+    };
     auto tile = [&](uint32_t w) {
         Tile t;
         uint32_t tm = 0, tn = 0;
         if (w < total) tile_of(w, g.grid, &tm, &tn);
         t.m0 = (int32_t)tm * kIL4Tile;
         t.n0 = (int32_t)tn * kIL4Tile;
-        const uint64_t sa = w < total ? (uint64_t)(g.M - t.m0) * g.lda_b : 0;
-        const uint64_t sb = w < total ? (uint64_t)(g.N - t.n0) * g.ldb_b : 0;
-        t.ra = make_rsrc_words(g.A + (int64_t)t.m0 * g.lda_b,
-                               (uint32_t)(sa > kOobOffset ? kOobOffset : sa));
-        t.rb = make_rsrc_words(g.B + (int64_t)t.n0 * g.ldb_b,
-                               (uint32_t)(sb > kOobOffset ? kOobOffset : sb));
+        t.ra = panel(kAT, g.A, g.lda_b, g.M, t.m0, w < total);
+        t.rb = panel(kBT, g.B, g.ldb_b, g.N, t.n0, w < total);
         return t;
     };
     // Load i (0-7: A block wave+4i, 8-15: B block wave+4(i-8)) of stage s of
@@ -390,12 +425,21 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s, int i) {
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
+        const bool km = i < 8 ? kAT : kBT;
+        const uint32_t ld_b = i < 8 ? g.lda_b : g.ldb_b;
         uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
-        if constexpr (decltype(masked)::value) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
-        if (i < 8)
-            load_lds_b128(tt.ra, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
-        else
-            load_lds_b128(tt.rb, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
+        uint32_t so = koff;
+        if (km) {
+            // K-rows past K fall outside the buffer and read zeros.  The
+            // stage's K-row offset goes into the VGPR offset: the buffer
+            // range check does not count the SGPR offset.
+            vo += s * kKMStageRows * ld_b;
+            so = 0;
+        } else if constexpr (decltype(masked)::value) {
+            vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
+        }
+        load_lds_b128(i < 8 ? tt.ra : tt.rb, (HK_LDS void*)((i < 8 ? d.a : d.b) + blk * 64u), vo,
+                      so);
     };
 
     // ---- LDS -> fragments.  Slice s of a 16-row block: lane l holds 8 bf16
@@ -406,8 +450,29 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     const uint32_t fo1 = r16 * kChunks + ((4u + g4) ^ (r16 & 7u));
     const uint32_t arow = wm * 128u;
     const uint32_t brow = wn * 128u;
+    // transposed image: lane l (group g4, i = l%16, a = i%4, r = i/4) addresses
+    // K-row 8 g4 + r (+ 32s + 4h), rows 4a .. 4a+3 of the block: chunk
+    // 2 (block base / 16) + a/2 of that K-row, byte 8 (a%2).  km_key of those
+    // K-rows is 2 (r | g4 << 2) for every s and h.
+    const uint32_t km_a = lane & 3u;
+    const uint32_t km_kk = ((lane >> 2) & 3u) | (g4 << 2);
+    const uint32_t km_row =
+        (8u * g4 + ((lane >> 2) & 3u)) * kKMRowBytes + (km_a & 1u) * 8u + (km_a >> 1) * 16u;
+    auto read_km = [&](const HK_LDS i32x4* img, int s, uint32_t blk16) -> i32x4 {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const HK_LDS uint8_t* p = (const HK_LDS uint8_t*)img + km_row + 32u * (blk16 ^ km_kk) +
+                                  (uint32_t)(32 * s) * kKMRowBytes;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((HK_LDS s16x4*)p);
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((HK_LDS s16x4*)(p + 4u * kKMRowBytes));
+        return __builtin_shufflevector(__builtin_bit_cast(i32x2, lo), __builtin_bit_cast(i32x2, hi),
+                                       0, 1, 2, 3);
+    };
     // fragment f of slice s: f = 0..7 A blocks, 8..15 B blocks
     auto read = [&](const IL4Buf& d, int s, int f) -> i32x4 {
+        if (f < 8 ? kAT : kBT)
+            return read_km(f < 8 ? d.a : d.b, s,
+                           f < 8 ? arow / 16u + (uint32_t)f : brow / 16u + (uint32_t)(f - 8));
         const HK_LDS i32x4* base = f < 8 ? d.a + (arow + 16u * (uint32_t)f) * kChunks
                                          : d.b + (brow + 16u * (uint32_t)(f - 8)) * kChunks;
         return base[s == 0 ? fo0 : fo1];
@@ -1357,8 +1422,10 @@ __device__ __forceinline__ void basic_body(const GemmArgs& g, HK_LDS i32x4* sA, 
             for (uint32_t e = 0; e < 32; ++e) {
                 const int64_t k = k0 + lb + e;
                 uint8_t va = 0, vb = 0;
-                if (am < g.M && k < g.K) va = g.A[(int64_t)am * g.lda_b + k];
-                if (bn < g.N && k < g.K) vb = g.B[(int64_t)bn * g.ldb_b + k];
+                if (am < g.M && k < g.K)
+                    va = g.a_t ? g.A[k * g.lda_b + am] : g.A[(int64_t)am * g.lda_b + k];
+                if (bn < g.N && k < g.K)
+                    vb = g.b_t ? g.B[k * g.ldb_b + bn] : g.B[(int64_t)bn * g.ldb_b + k];
                 sAb[lr * kRowBytes + lb + e] = va;
                 sBb[lr * kRowBytes + lb + e] = vb;
             }
@@ -1370,8 +1437,8 @@ __device__ __forceinline__ void basic_body(const GemmArgs& g, HK_LDS i32x4* sA, 
             for (uint32_t e = 0; e < 16; ++e) {
                 const int64_t k = k0 + lb / 2 + e;
                 uint16_t va = 0, vb = 0;
-                if (am < g.M && k < g.K) va = A16[(int64_t)am * lda + k];
-                if (bn < g.N && k < g.K) vb = B16[(int64_t)bn * ldb + k];
+                if (am < g.M && k < g.K) va = g.a_t ? A16[k * lda + am] : A16[(int64_t)am * lda + k];
+                if (bn < g.N && k < g.K) vb = g.b_t ? B16[k * ldb + bn] : B16[(int64_t)bn * ldb + k];
                 ((HK_LDS uint16_t*)sAb)[(lr * kRowBytes + lb) / 2 + e] = va;
                 ((HK_LDS uint16_t*)sBb)[(lr * kRowBytes + lb) / 2 + e] = vb;
             }

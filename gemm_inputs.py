@@ -24,7 +24,15 @@ Workloads (M x N x K, operands K-contiguous, A is M x K, B is N x K):
                       rounded to e4m3 (the conversion of the OCP MX v1.0
                       specification);
 * ``bf16_mlp_shard8`` 8192 x 3584 x 8192: one GPU's share of the MLP shape
-                      split eight ways along N.
+                      split eight ways along N;
+* ``bf16_8192_bkn``   the bf16_8192 matrices with B stored K x N (C = A B);
+* ``bf16_8192_akm_bkn`` the same with A stored K x M as well (C = A^T B with
+                      the stored arrays).
+
+Stored operands: a workload's layout_a / layout_b say how A and B sit in
+memory (0: rows of K, A as M x K and B as N x K; 1: A as K x M, B as K x N).
+make_inputs returns the logical M x K and N x K matrices, whatever the layout;
+stored() gives the arrays as the layout stores them.
 
 Seeds: workload index c gives A seed 1000c+1 and B seed 1000c+2; the integer
 variant adds 10.
@@ -48,6 +56,16 @@ class Workload:
     K: int
     dtype: str   # "bf16", "fp8" or "mxfp8"
     dist: str    # "uniform", "normal", "normal002", "int4", "fp8_normal"
+    layout_a: int = 0  # 1: A stored K x M
+    layout_b: int = 0  # 1: B stored K x N
+
+    @property
+    def lda(self) -> int:
+        return self.M if self.layout_a else self.K
+
+    @property
+    def ldb(self) -> int:
+        return self.N if self.layout_b else self.K
 
     @property
     def flops(self) -> float:
@@ -80,6 +98,8 @@ WORKLOADS = {
         # tiles of 256 x 256: 1.75 windows of 256 co-resident workgroups)
         Workload("bf16_mlp_shard8", 3, 8192, 3584, 8192, "bf16", "normal002"),
         Workload("mxfp8_8192", 5, 8192, 8192, 8192, "mxfp8", "mx_normal"),
+        Workload("bf16_8192_bkn", 2, 8192, 8192, 8192, "bf16", "normal002", 0, 1),
+        Workload("bf16_8192_akm_bkn", 2, 8192, 8192, 8192, "bf16", "normal002", 1, 1),
     ]
 }
 
@@ -174,6 +194,14 @@ def make_inputs(w: Workload, integer: bool = False):
     A, sa = fp8_matrix(w.M, w.K, sa_seed, integer)
     B, sb = fp8_matrix(w.N, w.K, sb_seed, integer)
     return {"A": A, "B": B, "scale_a": sa, "scale_b": sb}
+
+
+def stored(w: Workload, x: dict):
+    """(A, B) as the workload's layout stores them: the logical M x K and N x K
+    matrices, or their transposes (K x M, K x N) for a layout of 1."""
+    A = x["A"].t().contiguous() if w.layout_a else x["A"]
+    B = x["B"].t().contiguous() if w.layout_b else x["B"]
+    return A, B
 
 
 def bits(t: torch.Tensor):

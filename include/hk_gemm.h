@@ -12,6 +12,8 @@
  * for 0 <= i < M, 0 <= j < N, with FP32 accumulation.  A is M x K and B is
  * N x K, both row-major with K contiguous (so B is used transposed), C is
  * M x N row-major.  s = 1 for BF16 inputs, s = scale_a * scale_b for FP8.
+ * hk_gemm_ex also takes either operand stored the other way round (K x M,
+ * K x N: hk_layout below), which gives A * B, A^T * B^T and A^T * B.
  *
  * Element types.  BF16: 16-bit bfloat16 bit patterns.  FP8: OCP E4M3FN bytes
  * (bias 7, largest finite 448, S.1111.111 is NaN), one fp32 scale per tensor
@@ -30,7 +32,8 @@
  * Arguments are validated before any HIP call; invalid ones return
  * HK_ERROR_INVALID_VALUE and enqueue nothing: negative M, N or K; a NULL
  * pointer for an operand that would be read or written; lda < K or ldb < K
- * (when K > 0); ldc < N; an unknown dtype, schedule or grid order; a
+ * (when K > 0; lda < M or ldb < N for an operand stored K-strided); ldc < N;
+ * an unknown dtype, schedule, grid order or layout; a
  * non-finite scale.  M == 0 or N == 0 is a no-op success.  K == 0 writes
  * zeros to C (the empty sum is +0).  A failure reported by the HIP runtime at
  * launch returns HK_ERROR_LAUNCH.  HK_ERROR_NOT_SUPPORTED is returned when an
@@ -113,13 +116,36 @@ typedef enum hk_grid_order {
     HK_GRID_XCD = 2
 } hk_grid_order;
 
+/*
+ * Storage of an operand.  The GeekNews summary "HipKittens: fast and furious
+ * AMD kernels" (section "Real kernel example") lists mma_AtB among the tile
+ * operations of the hot loops, i.e. products with a transposed operand; the
+ * page fixes no global layout, so both are offered for each operand:
+ *   K_CONTIGUOUS  A(i, k) = A[i*lda + k] (A stored M x K), B(j, k) =
+ *                 B[j*ldb + k] (B stored N x K): the default, lda, ldb >= K;
+ *   K_STRIDED     A(i, k) = A[k*lda + i] (A stored K x M, lda >= M),
+ *                 B(j, k) = B[k*ldb + j] (B stored K x N, ldb >= N).
+ * C = sum_k A(i, k) B(j, k) in every case: A K_STRIDED gives A^T-style
+ * products, B K_STRIDED gives C = A * B with B as stored, and both give the
+ * pages' A^T * B.  K_STRIDED runs on INTERLEAVE4 (BF16; chosen by AUTO) or
+ * BASIC.  INTERLEAVE4 needs, per K_STRIDED operand, 16-byte alignment, the
+ * stride and M (or N) multiples of 8, and (K + 128) rows of stride below
+ * 2^31 bytes; the other schedules return HK_ERROR_NOT_SUPPORTED for it.
+ */
+typedef enum hk_layout {
+    HK_LAYOUT_K_CONTIGUOUS = 0,
+    HK_LAYOUT_K_STRIDED = 1
+} hk_layout;
+
 /* Optional knobs for hk_gemm_ex.  Zero-initialise for the defaults. */
 typedef struct hk_gemm_opts {
     int32_t schedule;    /* hk_schedule */
     int32_t grid_order;  /* hk_grid_order */
     int32_t group_m;     /* tile rows per group in the XCD order; 0 = default */
     int32_t window;      /* co-resident workgroups per window; 0 = CU count */
-    int32_t reserved[4]; /* must be zero */
+    int32_t layout_a;    /* hk_layout of A */
+    int32_t layout_b;    /* hk_layout of B */
+    int32_t reserved[2]; /* must be zero */
 } hk_gemm_opts;
 
 /* What a call with these arguments would launch (filled by hk_gemm_plan). */

@@ -85,10 +85,85 @@ def test_ex_rejects_bad_dtype_and_options(L):
         st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
                           ctypes.byref(o), None)
         assert st == hk.HK_ERROR_INVALID_VALUE, field
+    for field, val in [("layout_a", 2), ("layout_b", -1)]:
+        o = hk.GemmOpts()
+        setattr(o, field, val)
+        st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
+                          ctypes.byref(o), None)
+        assert st == hk.HK_ERROR_INVALID_VALUE, field
     o = hk.GemmOpts()
-    o.reserved[2] = 1
+    o.reserved[1] = 1
     st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0, ctypes.byref(o), None)
     assert st == hk.HK_ERROR_INVALID_VALUE
+
+
+def test_opts_struct_matches_the_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct hk_gemm_opts \{(.*?)\} hk_gemm_opts;", text, re.S).group(1)
+    fields = re.findall(r"int32_t (\w+)(?:\[(\d+)\])?;", body)
+    assert [(n, int(c or 1)) for n, c in fields] == [
+        (n, getattr(t, "_length_", 1)) for n, t in hk.GemmOpts._fields_]
+    assert ctypes.sizeof(hk.GemmOpts) == 32
+
+
+# Operand layouts: K_STRIDED stores A as K x M (lda >= M) and B as K x N (ldb >= N).
+def test_strided_layout_leading_dimension_checks(L):
+    def ex(M, N, K, lda, ldb, la, lb):
+        o = hk._opts(layout_a=la, layout_b=lb)
+        return L.hk_gemm_ex(0, FAKE, FAKE, FAKE, M, N, K, lda, ldb, N, 1.0, 1.0, ctypes.byref(o),
+                            None)
+    # B stored K x N: ldb counts columns of B (N), not K
+    assert ex(32, 48, 64, 64, 47, 0, 1) == hk.HK_ERROR_INVALID_VALUE
+    # A stored K x M: lda counts M
+    assert ex(40, 32, 64, 39, 64, 1, 0) == hk.HK_ERROR_INVALID_VALUE
+    assert ex(40, 32, 64, 64, 63, 1, 0) == hk.HK_ERROR_INVALID_VALUE
+
+
+def test_plan_strided_layouts():
+    M, N, K = 8192, 8192, 8192
+    names = {(0, 0): "hk_gemm_il4_bf16", (1, 0): "hk_gemm_il4_bf16_akm",
+             (0, 1): "hk_gemm_il4_bf16_bkn", (1, 1): "hk_gemm_il4_bf16_akm_bkn"}
+    for (la, lb), name in names.items():
+        p = _plan(hk.HK_DTYPE_BF16, M, N, K, lda=M if la else K, ldb=N if lb else K,
+                  layout_a=la, layout_b=lb)
+        assert p["kernel_name"] == name and p["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4
+        assert p["workgroups"] == 256
+    # ldb below K is fine for B stored K x N (it counts N)
+    p = _plan(hk.HK_DTYPE_BF16, 512, 256, 1024, ldb=256, layout_b="k_strided")
+    assert p["kernel_name"] == "hk_gemm_il4_bf16_bkn"
+    # small outputs keep the 4-wave kernel (the small-tile kernel has no K-strided images)
+    p = _plan(hk.HK_DTYPE_BF16, 256, 256, 256, layout_b="k_strided")
+    assert p["kernel_name"] == "hk_gemm_il4_bf16_bkn"
+    # both operands K-strided: K needs no chunk alignment
+    p = _plan(hk.HK_DTYPE_BF16, 256, 256, 100, lda=256, ldb=256, layout_a=1, layout_b=1)
+    assert p["kernel_name"] == "hk_gemm_il4_bf16_akm_bkn"
+
+
+@pytest.mark.parametrize("case", [
+    dict(N=260, ldb=260),           # N of a K-strided B not whole 16-byte chunks
+    dict(ldb=264 + 4),              # stride not whole chunks
+    dict(B=FAKE + 8),               # B not 16-byte aligned
+    dict(K=100),                    # K-contiguous A with K not whole chunks
+    dict(K=1 << 20, ldb=1 << 10),   # (K + 128) rows of B past the 31-bit offsets
+], ids=lambda c: ",".join(c))
+def test_plan_strided_layout_falls_back_to_basic(case):
+    a = dict(M=512, N=256, K=1024, ldb=256, B=FAKE)
+    a.update(case)
+    p = _plan(hk.HK_DTYPE_BF16, a["M"], a["N"], a["K"], ldb=a["ldb"], B=a["B"], layout_b=1)
+    assert p["kernel_name"] == "hk_gemm_basic_bf16"
+
+
+def test_plan_strided_layout_other_schedules_unsupported():
+    for sched in ("pingpong8", "smalltile", "interleave8", "producer_consumer"):
+        with pytest.raises(hk.HKError):
+            _plan(hk.HK_DTYPE_BF16, 1024, 1024, 1024, schedule=sched, layout_a=1, lda=1024)
+    # FP8 with a K-strided operand: the plain kernel only
+    p = _plan(hk.HK_DTYPE_FP8_E4M3, 1024, 1024, 1024, layout_b=1, ldb=1024)
+    assert p["kernel_name"] == "hk_gemm_basic_fp8"
+    with pytest.raises(hk.HKError):
+        _plan(hk.HK_DTYPE_FP8_E4M3, 1024, 1024, 1024, layout_b=1, ldb=1024, schedule="interleave4")
+    p = _plan(hk.HK_DTYPE_BF16, 1024, 1024, 1024, layout_b=1, ldb=1024, schedule="basic")
+    assert p["kernel_name"] == "hk_gemm_basic_bf16"
 
 
 def _mx(L, **kw):
