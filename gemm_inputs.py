@@ -27,7 +27,8 @@ Workloads (M x N x K, operands K-contiguous, A is M x K, B is N x K):
                       split eight ways along N;
 * ``bf16_8192_bkn``   the bf16_8192 matrices with B stored K x N (C = A B);
 * ``bf16_8192_akm_bkn`` the same with A stored K x M as well (C = A^T B with
-                      the stored arrays).
+                      the stored arrays);
+* ``bf16_8192_akm``   the bf16_8192 matrices with A stored K x M only.
 
 Stored operands: a workload's layout_a / layout_b say how A and B sit in
 memory (0: rows of K, A as M x K and B as N x K; 1: A as K x M, B as K x N).
@@ -100,6 +101,7 @@ WORKLOADS = {
         Workload("mxfp8_8192", 5, 8192, 8192, 8192, "mxfp8", "mx_normal"),
         Workload("bf16_8192_bkn", 2, 8192, 8192, 8192, "bf16", "normal002", 0, 1),
         Workload("bf16_8192_akm_bkn", 2, 8192, 8192, 8192, "bf16", "normal002", 1, 1),
+        Workload("bf16_8192_akm", 2, 8192, 8192, 8192, "bf16", "normal002", 1, 0),
     ]
 }
 
