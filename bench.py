@@ -79,16 +79,20 @@ def traffic_from_profiles(kernel: str, workload: str):
     m2 = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m1 and m2):
         return None
-    return (m1.group(1), float(m2.group(1))) if m1.group(1) == kernel_source_sha() else None
+    return (m1.group(1), float(m2.group(1))) if m1.group(1) == kernel_source_sha(kernel) else None
 
 
-def kernel_source_sha() -> str:
+# The sources each kernel family is built from (its hash keys recorded traffic).
+KERNEL_SOURCES = {"hk_gemm": ("hk_device.hpp", "hk_gemm.hip", "hk_grid.hpp", "hk_kernels.hpp")}
+
+
+def kernel_source_sha(kernel: str = "hk_gemm") -> str:
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "fp8_gemm_02_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    family = next(k for k in KERNEL_SOURCES if kernel.startswith(k))
+    for f in sorted(KERNEL_SOURCES[family]):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
 
