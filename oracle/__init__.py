@@ -71,6 +71,9 @@ def _load():
     lib.oracle_gemm_mx_sampled.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                            vp, vp, i64, vp, vp, i32]
     lib.oracle_gemm_mx_sampled.restype = i32
+    lib.oracle_attn_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, f64, i32,
+                                    vp, i64, vp, vp, vp, vp, i32]
+    lib.oracle_attn_fwd.restype = i32
     _lib = lib
     return lib
 
@@ -299,3 +302,49 @@ def compare(c_gpu_bits, c_ref_bits, S=None, exact: bool = False, rel_tol: float 
         idx = int(np.flatnonzero(bad)[0])
         stats["first_bad"] = (idx, int(g[idx]), int(r[idx]), float(S[idx]))
     return stats
+
+
+def _strides(s, H, N, D):
+    """(batch, head, token) strides in elements; None = packed B x H x N x D."""
+    if s is None:
+        s = (H * N * D, N * D, D)
+    return np.ascontiguousarray(s, dtype=np.int64)
+
+
+def attention(Q, K, V, B: int, Hq: int, Hkv: int, N: int, D: int, scale: float,
+              causal: bool, q_strides=None, k_strides=None, v_strides=None, rows=None,
+              threads: int | None = None):
+    """Attention forward on bf16 bit patterns (uint16 arrays).
+
+    Q is B x Hq x N x D, K and V are B x Hkv x N x D, with (batch, head, token)
+    strides in elements (None = packed).  rows: flattened query rows
+    (b * Hq + h) * N + i to compute, or None for all of them in order.
+    Returns (O bits (nrows, D) uint16, O as float64, LSE (nrows,), A (nrows, D))
+    where A = sum_j p_j |v_j| / sum_j p_j, the magnitude the tolerance uses.
+    """
+    Q = _as_bits(Q, BF16)
+    K = _as_bits(K, BF16)
+    V = _as_bits(V, BF16)
+    sq = _strides(q_strides, Hq, N, D)
+    sk = _strides(k_strides, Hkv, N, D)
+    sv = _strides(v_strides, Hkv, N, D)
+    for X, s, H in ((Q, sq, Hq), (K, sk, Hkv), (V, sv, Hkv)):
+        if B * H * N > 0 and X.size < (B - 1) * s[0] + (H - 1) * s[1] + (N - 1) * s[2] + D:
+            raise ValueError("operand too small for its shape and strides")
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+    else:
+        n = B * Hq * N
+    o = np.zeros((n, D), dtype=np.uint16)
+    o64 = np.zeros((n, D), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    amag = np.zeros((n, D), dtype=np.float64)
+    rc = _load().oracle_attn_fwd(Q.ctypes.data, K.ctypes.data, V.ctypes.data, B, Hq, Hkv, N, D,
+                                 sq.ctypes.data, sk.ctypes.data, sv.ctypes.data, float(scale),
+                                 int(bool(causal)), rows.ctypes.data if rows is not None else None,
+                                 n, o.ctypes.data, o64.ctypes.data, lse.ctypes.data,
+                                 amag.ctypes.data, threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_attn_fwd rejected its arguments (%d)" % rc)
+    return o, o64, lse, amag

@@ -29,6 +29,9 @@
  * Alongside C the oracle returns S[i][j] = |s| * sum_k |dec(a)*dec(b)|, the
  * magnitude sum that the tolerance |C_gpu - C_ref| <= ulp(C_ref) + 1e-4*S uses.
  *
+ * The file also holds the attention-forward oracle (its own section, at the
+ * end) and the MXFP8 product.
+ *
  * Pins (tests marked "not gpu"): integer-valued inputs against an int64
  * product, exact rational sums with fractions.Fraction on tiny shapes, an
  * identity B, the transpose identity, the e4m3 table against torch's
@@ -36,6 +39,7 @@
  * hand-derived fixtures under tests/golden/.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -368,4 +372,136 @@ int oracle_gemm_mx_sampled(const uint8_t *A, const uint8_t *B, const uint8_t *SA
             s_out[p] = m;
     }
     return 0;
+}
+
+/* ------------------------------------------------------------ attention
+ *
+ * Attention forward, the second workload of the pages ("How to make AMD GPUs
+ * go brrr", section "Real kernel example": its hot loop runs the same wave
+ * schedule as the BF16 GEMM; "HipKittens: fast and furious AMD kernels",
+ * section "Performance results": causal and non-causal, several head
+ * dimensions D and sequence lengths N).  The pages do not write the operation
+ * out; the oracle takes textbook scaled dot-product attention over BF16
+ * inputs, one query row at a time:
+ *
+ *     s_j   = scale * sum_{d<D} q[d] * k_j[d]      for j < N (j <= i if causal)
+ *     O_i   = RNE_bf16( sum_j exp(s_j - m) * v_j / sum_j exp(s_j - m) ),  m = max_j s_j
+ *     LSE_i = m + log(sum_j exp(s_j - m))
+ *
+ * Query head h reads key/value head h / (Hq / Hkv) (grouped-query attention:
+ * each key/value head serves Hq / Hkv consecutive query heads).  Element
+ * (b, h, t, d) of a tensor sits at b*s[0] + h*s[1] + t*s[2] + d.
+ *
+ * In double: exact products, ascending sums, one exp per score, one rounding
+ * to bf16 at the end.  Alongside O the oracle returns, per element,
+ * A = sum_j p_j |v_j[d]| / sum_j p_j, the magnitude the tolerance uses.
+ */
+static int check_args_attn(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t B,
+                           int64_t Hq, int64_t Hkv, int64_t N, int64_t D, const int64_t *sq,
+                           const int64_t *sk, const int64_t *sv)
+{
+    if (B < 0 || Hq < 1 || Hkv < 1 || N < 0 || D < 1 || Hq % Hkv != 0)
+        return 1;
+    if (Q == NULL || K == NULL || V == NULL || sq == NULL || sk == NULL || sv == NULL)
+        return 1;
+    return 0;
+}
+
+/* One query row r = (b * Hq + h) * N + i: O[0..D), and optionally its double
+ * values, LSE and A.  s is scratch for N scores. */
+static void attn_row(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t Hq,
+                     int64_t Hkv, int64_t N, int64_t D, const int64_t *sq, const int64_t *sk,
+                     const int64_t *sv, double scale, int causal, int64_t r, double *s,
+                     uint16_t *o, double *o64, double *lse, double *amag)
+{
+    const int64_t i = r % N;
+    const int64_t h = (r / N) % Hq;
+    const int64_t b = r / (N * Hq);
+    const int64_t kvh = h / (Hq / Hkv);
+    const int64_t nk = causal ? i + 1 : N;
+    const uint16_t *q = Q + b * sq[0] + h * sq[1] + i * sq[2];
+    double m = -INFINITY, l = 0.0;
+    int64_t j, d;
+
+    for (j = 0; j < nk; ++j) {
+        const uint16_t *kj = K + b * sk[0] + kvh * sk[1] + j * sk[2];
+        double acc = 0.0;
+        for (d = 0; d < D; ++d)
+            acc += oracle_bf16_decode(q[d]) * oracle_bf16_decode(kj[d]);
+        s[j] = scale * acc;
+        if (s[j] > m)
+            m = s[j];
+    }
+    for (j = 0; j < nk; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (d = 0; d < D; ++d) {
+        double acc = 0.0, mag = 0.0, val;
+        for (j = 0; j < nk; ++j) {
+            const double v = oracle_bf16_decode(V[b * sv[0] + kvh * sv[1] + j * sv[2] + d]);
+            acc += s[j] * v;
+            mag += s[j] * fabs(v);
+        }
+        val = acc / l;
+        o[d] = oracle_bf16_round(val);
+        if (o64)
+            o64[d] = val;
+        if (amag)
+            amag[d] = mag / l;
+    }
+    if (lse)
+        *lse = m + log(l);
+}
+
+/*
+ * Attention forward for the query rows listed in rows[0..nrows) (each
+ * (b * Hq + h) * N + i), or for every row (B * Hq * N of them, in that order)
+ * when rows is NULL.  Q is B x Hq x N x D, K and V are B x Hkv x N x D, with
+ * strides sq, sk, sv (batch, head, token; elements).  Outputs, nrows x D
+ * (nrows x 1 for lse): o (bf16 bits, required), o64, lse and amag (optional).
+ * Returns 0; 1 for invalid arguments (nothing written); 2 if scratch memory
+ * for the scores could not be allocated.
+ */
+int oracle_attn_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t B,
+                    int64_t Hq, int64_t Hkv, int64_t N, int64_t D, const int64_t *sq,
+                    const int64_t *sk, const int64_t *sv, double scale, int causal,
+                    const int64_t *rows, int64_t nrows, uint16_t *o, double *o64, double *lse,
+                    double *amag, int nthreads)
+{
+    const int64_t total = B * Hq * N;
+    int64_t p;
+    int failed = 0;
+
+    if (check_args_attn(Q, K, V, B, Hq, Hkv, N, D, sq, sk, sv) || o == NULL)
+        return 1;
+    if (rows == NULL)
+        nrows = total;
+    if (nrows < 0)
+        return 1;
+    if (rows)
+        for (p = 0; p < nrows; ++p)
+            if (rows[p] < 0 || rows[p] >= total)
+                return 1;
+    if (nthreads < 1)
+        nthreads = 1;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (s == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (p = 0; p < nrows; ++p) {
+            const int64_t r = rows ? rows[p] : p;
+            if (s)
+                attn_row(Q, K, V, Hq, Hkv, N, D, sq, sk, sv, scale, causal, r, s, o + p * D,
+                         o64 ? o64 + p * D : NULL, lse ? lse + p : NULL,
+                         amag ? amag + p * D : NULL);
+        }
+        free(s);
+    }
+    return failed ? 2 : 0;
 }

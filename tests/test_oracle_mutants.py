@@ -5,8 +5,12 @@ term, float accumulation, a transposed operand, a wrong e4m3 bias or sign,
 rounding twice, the wrong tie rule, a lost scale, a lost subnormal clamp, an
 ignored row stride; for MXFP8: the wrong block size or block index, the wrong
 scale bias, swapped scale arrays, a NaN scale read as finite, an ignored scale
+stride; for attention: a dropped scale, a causal mask that is off by one or
+missing, the wrong grouped-query head, no max shift, no log in the LSE, keys
+read as values, a dropped last key, rounding through float, an ignored head
 stride), builds the copy on the CPU in a temporary directory, and
-runs the pins of test_oracle.py and test_oracle_mx.py against it.  At least one pin must fail for
+runs the pins of test_oracle.py, test_oracle_mx.py and test_oracle_attn.py
+against it.  At least one pin must fail for
 every mutant.  The oracle itself is never modified.
 """
 import ctypes
@@ -17,6 +21,7 @@ import pytest
 
 import oracle
 from tests import test_oracle as pins
+from tests import test_oracle_attn as attn_pins
 from tests import test_oracle_mx as mx_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
@@ -39,6 +44,19 @@ MUTANTS = {
     "mx_scales_swapped": ("xtab[SA[i * ldsa + k / 32]]", "xtab[SB[i * ldsb + k / 32]]"),
     "mx_nan_scale_ignored": ("if (x == 255)\n        return NAN;", "if (x == 255)\n        return 1.0;"),
     "mx_ignored_ldsa": ("SA[i * ldsa + k / 32]", "SA[i * ((K + 31) / 32) + k / 32]"),
+    "attn_no_scale": ("s[j] = scale * acc;", "s[j] = acc;"),
+    "attn_causal_strict": ("causal ? i + 1 : N", "causal ? i : N"),
+    "attn_causal_ignored": ("causal ? i + 1 : N", "N"),
+    "attn_gqa_modulo": ("h / (Hq / Hkv)", "h % Hkv"),
+    "attn_no_max_shift": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j]);"),
+    "attn_lse_no_log": ("*lse = m + log(l);", "*lse = m + l;"),
+    "attn_keys_as_values": ("V[b * sv[0] + kvh * sv[1] + j * sv[2] + d]",
+                            "K[b * sk[0] + kvh * sk[1] + j * sk[2] + d]"),
+    "attn_dropped_last_key": ("for (j = 0; j < nk; ++j) {\n            const double v",
+                              "for (j = 0; j + 1 < nk; ++j) {\n            const double v"),
+    "attn_rounded_through_float": ("o[d] = oracle_bf16_round(val);",
+                                   "o[d] = oracle_bf16_round((double)(float)val);"),
+    "attn_ignored_head_stride": ("h * sq[1]", "h * D"),
 }
 
 PINS = [
@@ -60,6 +78,16 @@ PINS = [
     mx_pins.test_block_boundaries,
     mx_pins.test_nan_scale_poisons_its_row_only,
     mx_pins.test_strided_equals_packed,
+    lambda m: attn_pins.test_matches_torch_sdpa_float64(m, 2, 4, 2, 7, 8, False),
+    lambda m: attn_pins.test_matches_torch_sdpa_float64(m, 2, 4, 2, 7, 8, True),
+    lambda m: attn_pins.test_correctly_rounded_against_mpmath(m, 0, True),
+    lambda m: attn_pins.test_zero_queries_give_the_mean_of_visible_values(m, True),
+    attn_pins.test_mean_that_double_rounding_gets_wrong,
+    attn_pins.test_single_key_returns_its_value_row,
+    attn_pins.test_first_causal_row_sees_only_key_zero,
+    attn_pins.test_dominant_key_gives_its_value_row,
+    attn_pins.test_grouped_query_heads_equal_repeated_heads,
+    attn_pins.test_strided_equals_packed,
 ]
 
 
