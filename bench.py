@@ -83,7 +83,8 @@ def traffic_from_profiles(kernel: str, workload: str):
 
 
 # The sources each kernel family is built from (its hash keys recorded traffic).
-KERNEL_SOURCES = {"hk_gemm": ("hk_device.hpp", "hk_gemm.hip", "hk_grid.hpp", "hk_kernels.hpp")}
+KERNEL_SOURCES = {"hk_gemm": ("hk_device.hpp", "hk_gemm.hip", "hk_grid.hpp", "hk_kernels.hpp"),
+                  "hk_attn": ("hk_device.hpp", "hk_attn.hip", "hk_attn.hpp")}
 
 
 def kernel_source_sha(kernel: str = "hk_gemm") -> str:
@@ -152,6 +153,9 @@ def main():
     import gemm_inputs
     import fp8_gemm_02_amd as hk
 
+    if a.workload in gemm_inputs.ATTN_WORKLOADS:
+        bench_attn(a, gemm_inputs.ATTN_WORKLOADS[a.workload])
+        return
     w = gemm_inputs.WORKLOADS[a.workload]
     print("[bench] workload %s M=%d N=%d K=%d %s" % (w.name, w.M, w.N, w.K, w.dtype),
           file=sys.stderr, flush=True)
@@ -282,6 +286,112 @@ def main():
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_attn(w, x, seconds: float):
+    """The attention oracle, untuned, on whole query rows; scaled to TFLOP/s."""
+    import numpy as np
+    import oracle
+    import gemm_inputs
+    threads = oracle.default_threads()
+    q, k, v = (gemm_inputs.bits(x[n]).ravel() for n in "qkv")
+    nrow = w.B * w.Hq * w.N
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        rows = rng.integers(0, nrow, n)
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, w.B, w.Hq, w.Hkv, w.N, w.D, w.scale, w.causal, rows=rows,
+                         threads=threads)
+        t = time.perf_counter() - t0
+        keys = (rows % w.N + 1) if w.causal else np.full(n, w.N)
+        return t, 4.0 * w.D * float(keys.sum())
+
+    t, _ = run(threads)
+    n = int(max(threads, min(nrow, seconds / max(t / threads, 1e-9))))
+    t, flops = run(n)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": "%d random query rows of %d (all their visible keys), FP64 scalar oracle, "
+                      "%.1f s" % (n, nrow, t)}
+
+
+def bench_attn(a, w):
+    """Attention forward: one step is one hk_attn_fwd_bf16 launch (O and LSE)."""
+    import torch
+    import gemm_inputs
+    import fp8_gemm_02_amd as hk
+    print("[bench] workload %s B=%d Hq=%d Hkv=%d N=%d D=%d causal=%d" %
+          (w.name, w.B, w.Hq, w.Hkv, w.N, w.D, w.causal), file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = gemm_inputs.make_attn_inputs(w)
+    q, k, v = (x[n].to(dev) for n in "qkv")
+    O = torch.empty((w.B, w.Hq, w.N, w.D), dtype=torch.bfloat16, device=dev)
+    L = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    kernel = "hk_attn_fwd_d%d%s" % (w.D, "_causal" if w.causal else "")
+
+    def step():
+        hk.hk_attn_fwd_bf16(q, k, v, O, L, w.B, w.Hq, w.Hkv, w.N, w.D, w.scale, w.causal,
+                            stream=stream)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(a.warmup):
+            step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done (%d steps), timing %d" % (a.warmup, a.steps), file=sys.stderr,
+          flush=True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(a.steps):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    durs_ms = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
+    mean_ms = sum(durs_ms) / len(durs_ms)
+    value = w.flops * a.steps / elapsed / 1e12
+    achieved = w.flops / (mean_ms * 1e-3) / 1e12
+    tr = traffic_from_profiles(kernel, w.name)
+    out = {
+        "metric": "attention forward TFLOP/s, BF16 B=%d Hq=%d Hkv=%d N=%d D=%d %s (1 MI355X)"
+                  % (w.B, w.Hq, w.Hkv, w.N, w.D, "causal" if w.causal else "non-causal"),
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(elapsed / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "D": w.D,
+                   "causal": w.causal, "layout": "B x H x N x D packed",
+                   "distribution": "normal", "kernel": kernel,
+                   "flops_counted": "4 * D per visible (query, key) pair"},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 2),
+        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(durs_ms[len(durs_ms) // 2], 4),
+                      "min": round(durs_ms[0], 4), "max": round(durs_ms[-1], 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": tr[1] if tr else None,
+                     "arithmetic_intensity": round(w.flops / w.algorithmic_bytes, 1),
+                     "algorithmic_flops_per_launch": w.flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+        "inputs": {n + "_sha256": gemm_inputs.sha256(x[n]) for n in "qkv"},
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_attn(w, x, a.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -46,7 +46,7 @@ GRID_ORDERS = {"auto": 0, "row_major": 1, "xcd": 2}
 LAYOUTS = {"k_contiguous": 0, "k_strided": 1}
 
 EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-            "hk_grid_map", "hk_status_string", "hk_version")
+            "hk_grid_map", "hk_status_string", "hk_version", "hk_attn_fwd_bf16")
 
 
 class HKError(RuntimeError):
@@ -60,6 +60,12 @@ class GemmOpts(ctypes.Structure):
                 ("group_m", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
                 ("reserved", ctypes.c_int32 * 2)]
+
+
+class AttnStrides(ctypes.Structure):
+    """(batch, head, token) strides in elements of Q, K, V and O."""
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3),
+                ("v", ctypes.c_int64 * 3), ("o", ctypes.c_int64 * 3)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -101,8 +107,10 @@ def lib():
     L.hk_status_string.argtypes = [i32]
     L.hk_status_string.restype = ctypes.c_char_p
     L.hk_version.argtypes = []
+    L.hk_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32,
+                                   ctypes.POINTER(AttnStrides), vp]
     for name in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-                 "hk_grid_map", "hk_version"):
+                 "hk_grid_map", "hk_version", "hk_attn_fwd_bf16"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -268,3 +276,42 @@ def matmul(A, B, scale_a=None, scale_b=None, out=None, stream=None, **opts):
                1.0 if scale_a is None else scale_a, 1.0 if scale_b is None else scale_b,
                layout_a=la, layout_b=lb, stream=stream, **opts)
     return out
+
+
+def hk_attn_fwd_bf16(Q, K, V, O, lse, B, Hq, Hkv, N, D, scale, causal, strides=None,
+                     stream=None, raise_on_error=True):
+    """Attention forward (include/hk_attn.h).  strides: None (packed B x H x N x D)
+    or four (batch, head, token) stride triples for Q, K, V, O in elements."""
+    st = None
+    if strides is not None:
+        st = AttnStrides()
+        for name, tri in zip("qkvo", strides):
+            getattr(st, name)[:] = [int(x) for x in tri]
+    rc = lib().hk_attn_fwd_bf16(_ptr(Q), _ptr(K), _ptr(V), _ptr(O),
+                                _ptr(lse) if lse is not None else None, B, Hq, Hkv, N, D,
+                                float(scale), int(bool(causal)),
+                                ctypes.byref(st) if st is not None else None, _stream(stream))
+    return _check(rc, "hk_attn_fwd_bf16", raise_on_error)
+
+
+def attention(q, k, v, causal=False, scale=None, return_lse=False, out=None, stream=None):
+    """softmax(scale * q k^T [+ causal mask]) v for torch bf16 device tensors of
+    shape (B, Hq, N, D) and (B, Hkv, N, D) with D contiguous (any strides
+    otherwise; a (B, N, H, D) tensor seen through .transpose(1, 2) works).
+    Returns O (B, Hq, N, D), and the fp32 log-sum-exp (B, Hq, N) if asked."""
+    import torch
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, D) or v.shape != k.shape:
+        raise ValueError("k and v must be (B, Hkv, N, D) with q's B, N and D")
+    for t in (q, k, v):
+        if t.stride(3) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    if out is None:
+        out = torch.empty((B, Hq, N, D), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if return_lse else None
+    scale = D ** -0.5 if scale is None else scale
+    strides = [t.stride()[:3] for t in (q, k, v, out)]
+    hk_attn_fwd_bf16(q, k, v, out, lse, B, Hq, Hkv, N, D, scale, causal, strides=strides,
+                     stream=stream)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,303 @@
+// hk_attn.hpp -- attention forward on gfx950: O = softmax(scale * Q K^T
+// [+ causal mask]) V over BF16 Q, K, V, FP32 softmax and accumulation, BF16 O.
+//
+// The pages' second workload ("How to make AMD GPUs go brrr", section "Real
+// kernel example": the attention-forward hot loop runs on the same wave
+// schedules as the BF16 GEMM and uses exp2 and column sums; "HipKittens: fast
+// and furious AMD kernels", section "Performance results": causal and
+// non-causal, several head dimensions and sequence lengths).
+//
+// One workgroup of 4 waves takes 128 query rows of one (batch, head); each
+// wave owns 32 of them (two 16-row blocks) and keeps their Q fragments in
+// registers.  Keys and values stream through LDS in blocks of 64 (direct
+// HBM->LDS loads, two buffers), and each block updates the running softmax
+// (online: running max m and sum l per query, in log2 units, the output
+// rescaled by exp2(m_old - m_new)).
+//
+// Everything is computed transposed, which keeps every per-query quantity in
+// one lane and the probabilities in the registers that produced them:
+//
+//   S^T (keys x queries) = K Q^T    16x16x32 MFMA, "A" = K rows, "B" = Q rows:
+//                                   lane l holds query l%16, keys 4(l/16)..+3
+//   O^T (d x queries)   += V^T P^T  "A" = V^T (transposing LDS reads of V),
+//                                   "B" = P^T: lane l's 8 K-slots are its own
+//                                   probabilities of two 16-key blocks
+//
+// so the result lane l holds query l%16, d = 4(l/16)..+3: four consecutive
+// outputs of one row, stored as one 8-byte write.  The row max needs two
+// cross-lane exchanges per block (the four lanes that share a query); the row
+// sum stays per lane until the end.
+//
+// Two workgroups share a compute unit (2 waves per SIMD), so one wave's
+// softmax arithmetic runs while the other's matrix instructions do.
+#pragma once
+
+#include "hk_device.hpp"
+
+namespace hk {
+
+struct AttnArgs {
+    const uint16_t* Q;
+    const uint16_t* K;
+    const uint16_t* V;
+    uint16_t* O;
+    float* lse;          // optional: B x Hq x N, natural log
+    int32_t B, Hq, Hkv, N;
+    int32_t nqb;         // query blocks of 128 per (batch, head)
+    int32_t group;       // Hq / Hkv
+    float c;             // scale * log2(e)
+    int64_t sq[3], sk[3], sv[3], so[3];  // (batch, head, token) strides, elements
+};
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnQ = 128;   // query rows per workgroup
+constexpr int kAttnKV = 64;   // keys per block
+
+// LDS image of one block of K or V: 64 rows (keys) x D bf16, 16-byte chunk c
+// of row r at physical chunk c ^ key(r).
+//  K (read by rows: 16 lanes, 16 rows, one chunk): the key spreads 16 rows
+//  over all 64 banks.
+//  V (transposing reads: a half-wave touches 8 consecutive rows, 32 bytes
+//  each, at one chunk pair): the key, even, permutes chunk pairs so that
+//  those 8 rows land on distinct banks.
+template <int D>
+__device__ __forceinline__ uint32_t attn_kswz(uint32_t r) {
+    return D == 128 ? (r & 15u) : ((r >> 1) & 7u);
+}
+template <int D>
+__device__ __forceinline__ uint32_t attn_vswz(uint32_t r) {
+    return D == 128 ? 2u * (r & 7u) : 2u * ((r >> 1) & 3u);
+}
+
+// workgroup -> (batch * Hq + head, query block).  Workgroups are dealt to
+// the 8 chiplets round-robin; when the count allows, each chiplet gets a
+// contiguous range of heads, so that a head's K and V stay in one L2.
+// Within a head the query blocks run from the last (the most keys under a
+// causal mask) to the first.
+__device__ __forceinline__ void attn_tile_of(uint32_t w, uint32_t total, uint32_t nqb,
+                                             uint32_t* bh, uint32_t* qblk) {
+    uint32_t idx = w;
+    if (total % 8u == 0) idx = (w % 8u) * (total / 8u) + w / 8u;
+    *bh = idx / nqb;
+    *qblk = nqb - 1u - idx % nqb;
+}
+
+template <int D, bool kCausal>
+__device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t* lds) {
+    constexpr int kDC = D / 32;                    // 32-wide d chunks (S MFMAs)
+    constexpr int kDB = D / 16;                    // 16-wide d blocks (O MFMAs)
+    constexpr uint32_t kRowB = D * 2;              // bytes per K/V row
+    constexpr uint32_t kImgB = kAttnKV * kRowB;    // bytes per K or V block image
+    constexpr uint32_t kRowsPerLoad = 1024u / kRowB;
+    constexpr uint32_t kChunksPerRow = kRowB / 16u;
+    constexpr int kLoads = (int)(kAttnKV / (kRowsPerLoad * 4u));  // per thread per matrix
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t g4 = lane >> 4, r16 = lane & 15u;
+
+    uint32_t bh, qblk;
+    attn_tile_of(blockIdx.x, (uint32_t)(g.B * g.Hq) * (uint32_t)g.nqb, (uint32_t)g.nqb, &bh,
+                 &qblk);
+    const int32_t b = (int32_t)bh / g.Hq, h = (int32_t)bh % g.Hq;
+    const int32_t kvh = h / g.group;
+    const int32_t q0 = (int32_t)qblk * kAttnQ;
+    const int32_t q0w = q0 + 32 * (int32_t)wave;
+    const int32_t N = g.N;
+
+    // blocks of keys this workgroup needs
+    const int32_t kend = kCausal ? min(N, q0 + kAttnQ) : N;
+    const int32_t nblk = (kend + kAttnKV - 1) / kAttnKV;
+
+    // ---- Q fragments ("B" operand of S^T): lane l holds query q0w + 16qb +
+    // l%16, d = 32dc + 8(l/16) .. +7.  Rows past N read as zero.
+    i32x4 qf[2][kDC];
+    {
+        const uint16_t* Qh = g.Q + (int64_t)b * g.sq[0] + (int64_t)h * g.sq[1];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int32_t q = q0w + 16 * qb + (int32_t)r16;
+#pragma unroll
+            for (int dc = 0; dc < kDC; ++dc) {
+                qf[qb][dc] = i32x4{0, 0, 0, 0};
+                if (q < N)
+                    qf[qb][dc] = *reinterpret_cast<const i32x4*>(
+                        Qh + (int64_t)q * g.sq[2] + 32 * dc + 8 * (int32_t)g4);
+            }
+        }
+    }
+
+    // ---- K and V blocks: direct loads into LDS.  Buffer resources over the
+    // (batch, kv head) rows 0..N-1: rows past N read as zero.
+    const uint32_t ktok_b = (uint32_t)g.sk[2] * 2u, vtok_b = (uint32_t)g.sv[2] * 2u;
+    const i32x4 rk = make_rsrc_words(g.K + (int64_t)b * g.sk[0] + (int64_t)kvh * g.sk[1],
+                                     (uint32_t)((N - 1) * ktok_b + kRowB));
+    const i32x4 rv = make_rsrc_words(g.V + (int64_t)b * g.sv[0] + (int64_t)kvh * g.sv[1],
+                                     (uint32_t)((N - 1) * vtok_b + kRowB));
+    // load i of a matrix: rows kRowsPerLoad * (wave + 4i) .. of the block;
+    // lane l -> row + l / kChunksPerRow, physical chunk l % kChunksPerRow
+    uint32_t voff_k[kLoads], voff_v[kLoads];
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+        const uint32_t row = kRowsPerLoad * (wave + 4u * i) + lane / kChunksPerRow;
+        const uint32_t pc = lane % kChunksPerRow;
+        voff_k[i] = row * ktok_b + ((pc ^ attn_kswz<D>(row)) * 16u);
+        voff_v[i] = row * vtok_b + ((pc ^ attn_vswz<D>(row)) * 16u);
+    }
+    auto issue = [&](int32_t j) {
+        HK_LDS uint8_t* kimg = lds + (uint32_t)(j & 1) * 2u * kImgB;
+        HK_LDS uint8_t* vimg = kimg + kImgB;
+        const uint32_t kb = (uint32_t)j * kAttnKV;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const uint32_t blk = wave + 4u * i;
+            // the block's row offset rides in the VGPR offset, which the
+            // buffer range check covers (the SGPR offset is not checked)
+            load_lds_b128(rk, (HK_LDS void*)(kimg + blk * 1024u), voff_k[i] + kb * ktok_b, 0u);
+            load_lds_b128(rv, (HK_LDS void*)(vimg + blk * 1024u), voff_v[i] + kb * vtok_b, 0u);
+        }
+    };
+
+    // ---- fragment reads
+    // K ("A" operand of S^T): key row 16kb + l%16, chunk 4dc + l/16
+    auto read_k = [&](const HK_LDS uint8_t* kimg, int kb, int dc) -> i32x4 {
+        const uint32_t r = 16u * kb + r16;
+        const uint32_t ch = (4u * dc + g4) ^ attn_kswz<D>(r);
+        return *(const HK_LDS i32x4*)(kimg + r * kRowB + ch * 16u);
+    };
+    // V^T ("A" operand of O^T) for d block db and keys 32c .. 32c+31: two
+    // transposing reads, of key rows 16(2c+hh) + 4(l/16) + r (r = (l/4)%4),
+    // d = 16db + 4(l%4) .. +3; output lane l gets d = 16db + l%16 and those
+    // four keys (measured lane map: within 16 lanes, output lane i's element
+    // r comes from source lane i/4 + 4r, position i%4).
+    const uint32_t va = lane & 3u, vr = (lane >> 2) & 3u;
+    auto read_vt = [&](const HK_LDS uint8_t* vimg, int db, int c) -> i32x4 {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        s16x4 part[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t r = 16u * (2u * c + hh) + 4u * g4 + vr;
+            const uint32_t ch = (2u * db + (va >> 1)) ^ attn_vswz<D>(r);
+            part[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (HK_LDS s16x4*)(vimg + r * kRowB + ch * 16u + (va & 1u) * 8u));
+        }
+        return __builtin_shufflevector(__builtin_bit_cast(i32x2, part[0]),
+                                       __builtin_bit_cast(i32x2, part[1]), 0, 1, 2, 3);
+    };
+
+    f32x4 o[kDB][2];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY};  // running max of S * c (log2 units)
+    float l[2] = {0.f, 0.f};              // this lane's share of the running sum
+
+    if (nblk > 0) issue(0);
+    for (int32_t j = 0; j < nblk; ++j) {
+        if (j + 1 < nblk) {
+            issue(j + 1);
+            wait_vmcnt<2 * kLoads>();  // block j has landed (this wave's part)
+        } else {
+            wait_vmcnt0();
+        }
+        fenced_barrier();  // ... and every wave's part
+        const HK_LDS uint8_t* kimg = lds + (uint32_t)(j & 1) * 2u * kImgB;
+        const HK_LDS uint8_t* vimg = kimg + kImgB;
+        const int32_t k0 = j * kAttnKV;
+
+        // a wave whose queries all lie before this block has nothing to add
+        if (!kCausal || k0 <= q0w + 31) {
+            // ---- S^T = K Q^T
+            f32x4 s[4][2];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int dc = 0; dc < kDC; ++dc) {
+                    const i32x4 kf = read_k(kimg, kb, dc);
+                    s[kb][0] = mfma_bf16_16x16x32(kf, qf[0][dc], s[kb][0]);
+                    s[kb][1] = mfma_bf16_16x16x32(kf, qf[1][dc], s[kb][1]);
+                }
+            }
+            // ---- online softmax, per query (lane l%16) in log2 units
+            const bool masked = (kCausal && k0 + kAttnKV - 1 > q0w) || k0 + kAttnKV > N;
+            i32x4 pf[2][2];  // P^T fragments: [qb][c]
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int32_t q = q0w + 16 * qb + (int32_t)r16;
+                float t[16];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        float x = s[kb][qb][v] * g.c;
+                        if (masked) {
+                            const int32_t key = k0 + 16 * kb + 4 * (int32_t)g4 + v;
+                            if ((kCausal && key > q) || key >= N) x = -INFINITY;
+                        }
+                        t[4 * kb + v] = x;
+                    }
+                float mx = t[0];
+#pragma unroll
+                for (int e = 1; e < 16; ++e) mx = fmaxf(mx, t[e]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mnew = fmaxf(m[qb], mx);
+                const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
+                m[qb] = mnew;
+                float p[16], sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    p[e] = __builtin_amdgcn_exp2f(t[e] - mnew);
+                    sum += p[e];
+                }
+                l[qb] = l[qb] * alpha + sum;
+#pragma unroll
+                for (int db = 0; db < kDB; ++db) o[db][qb] *= alpha;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const float* pc = p + 8 * c;
+                    pf[qb][c] = i32x4{(int)pack_bf16x2(pc[0], pc[1]), (int)pack_bf16x2(pc[2], pc[3]),
+                                      (int)pack_bf16x2(pc[4], pc[5]), (int)pack_bf16x2(pc[6], pc[7])};
+                }
+            }
+            // ---- O^T += V^T P^T
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const i32x4 vf = read_vt(vimg, db, c);
+                    o[db][0] = mfma_bf16_16x16x32(vf, pf[0][c], o[db][0]);
+                    o[db][1] = mfma_bf16_16x16x32(vf, pf[1][c], o[db][1]);
+                }
+        }
+        wait_lgkmcnt0();
+        fenced_barrier();  // every wave is done with this buffer
+    }
+
+    // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
+    uint16_t* Oh = g.O + (int64_t)b * g.so[0] + (int64_t)h * g.so[1];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float lt = l[qb];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const int32_t q = q0w + 16 * qb + (int32_t)r16;
+        if (q < N) {
+            const float inv = 1.0f / lt;
+            uint16_t* orow = Oh + (int64_t)q * g.so[2] + 4 * (int32_t)g4;
+#pragma unroll
+            for (int db = 0; db < kDB; ++db) {
+                const f32x4 v = o[db][qb] * inv;
+                *reinterpret_cast<uint2*>(orow + 16 * db) =
+                    make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+            }
+            if (g.lse && g4 == 0)
+                g.lse[((int64_t)b * g.Hq + h) * N + q] =
+                    (m[qb] + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
+        }
+    }
+}
+
+}  // namespace hk

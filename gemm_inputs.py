@@ -37,6 +37,9 @@ stored() gives the arrays as the layout stores them.
 
 Seeds: workload index c gives A seed 1000c+1 and B seed 1000c+2; the integer
 variant adds 10.
+
+Attention workloads (ATTN_WORKLOADS, make_attn_inputs) draw Q, K and V the
+same way, with seeds 1000c+1, +2, +3.
 """
 from __future__ import annotations
 
@@ -104,6 +107,66 @@ WORKLOADS = {
         Workload("bf16_8192_akm", 2, 8192, 8192, 8192, "bf16", "normal002", 1, 0),
     ]
 }
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """Attention forward: Q is B x Hq x N x D, K and V are B x Hkv x N x D
+    (packed, D contiguous), entries Normal(0, 1) rounded once to bf16,
+    softmax scale 1/sqrt(D)."""
+    name: str
+    index: int
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    D: int
+    causal: bool
+
+    @property
+    def scale(self) -> float:
+        return self.D ** -0.5
+
+    @property
+    def pairs(self) -> int:
+        """(query, key) pairs the mask leaves visible, per head."""
+        return self.N * (self.N + 1) // 2 if self.causal else self.N * self.N
+
+    @property
+    def flops(self) -> float:
+        """Two products of 2 * D FLOP per visible (query, key) pair."""
+        return 4.0 * self.B * self.Hq * self.pairs * self.D
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O (bf16) and the fp32 log-sum-exp written once."""
+        reads = 2 * self.B * (self.Hq + 2 * self.Hkv) * self.N * self.D
+        return reads + 2 * self.B * self.Hq * self.N * self.D + 4 * self.B * self.Hq * self.N
+
+
+# Sizes: the pages give none ("several head dimensions and sequence
+# lengths"); these are 16K tokens per launch at sequence length 4096 with a
+# model width of 2048 (16 heads of 128 or 32 of 64), and a grouped-query
+# shape (32 query heads over 8 key/value heads of 128) at 8192.
+ATTN_WORKLOADS = {
+    w.name: w for w in [
+        AttnWorkload("attn_d128_n4096", 20, 4, 16, 16, 4096, 128, False),
+        AttnWorkload("attn_d128_n4096_causal", 20, 4, 16, 16, 4096, 128, True),
+        AttnWorkload("attn_d64_n4096", 21, 4, 32, 32, 4096, 64, False),
+        AttnWorkload("attn_gqa_d128_n8192_causal", 22, 1, 32, 8, 8192, 128, True),
+    ]
+}
+
+
+def make_attn_inputs(w: AttnWorkload):
+    """dict(q, k, v) as packed bf16 CPU tensors; workload index c seeds q, k, v
+    with 1000c + 1, + 2, + 3."""
+    out = {}
+    for i, (name, H) in enumerate((("q", w.Hq), ("k", w.Hkv), ("v", w.Hkv))):
+        g = _gen(1000 * w.index + 1 + i)
+        out[name] = torch.randn(w.B, H, w.N, w.D, generator=g, dtype=torch.float32).to(
+            torch.bfloat16)
+    return out
 
 
 def _gen(seed: int) -> torch.Generator:

@@ -15,14 +15,18 @@ import fp8_gemm_02_amd as hk
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "hk_gemm.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced in these tests
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hk_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hk_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -33,7 +37,7 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-              "hk_grid_map", "hk_status_string", "hk_version"):
+              "hk_grid_map", "hk_status_string", "hk_version", "hk_attn_fwd_bf16"):
         assert n in names
     assert set(names) == set(hk.EXPORTED)
 
@@ -356,3 +360,46 @@ def test_interleave8_is_bf16_only():
     with pytest.raises(hk.HKError) as e:
         _plan(hk.HK_DTYPE_FP8_E4M3, 256, 256, 256, schedule="interleave8")
     assert e.value.status == hk.HK_ERROR_NOT_SUPPORTED
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn(L, **kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, O=FAKE, lse=None, B=1, Hq=4, Hkv=2, N=256, D=128,
+             scale=0.088, causal=0, strides=None)
+    a.update(kw)
+    st = a["strides"]
+    if st is not None:
+        s = hk.AttnStrides()
+        for name, tri in zip("qkvo", st):
+            getattr(s, name)[:] = tri
+        st = ctypes.byref(s)
+    return L.hk_attn_fwd_bf16(a["Q"], a["K"], a["V"], a["O"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                              a["N"], a["D"], a["scale"], a["causal"], st, None)
+
+
+@pytest.mark.parametrize("bad", [dict(B=-1), dict(Hq=-1), dict(N=-1), dict(Hkv=0), dict(Hq=3),
+                                 dict(D=0), dict(scale=float("nan")), dict(scale=float("inf")),
+                                 dict(Q=0), dict(K=0), dict(V=0), dict(O=0),
+                                 dict(strides=[(0, 0, 127), (0, 0, 128), (0, 0, 128), (0, 0, 128)]),
+                                 dict(strides=[(-8, 0, 128), (0, 0, 128), (0, 0, 128), (0, 0, 128)])],
+                         ids=lambda b: ",".join(b))
+def test_attn_invalid_arguments(L, bad):
+    assert _attn(L, **bad) == hk.HK_ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("unsupported", [dict(D=96), dict(D=256), dict(Q=FAKE + 8),
+                                         dict(O=FAKE + 2), dict(lse=FAKE + 2),
+                                         dict(strides=[(0, 0, 132), (0, 0, 128), (0, 0, 128),
+                                                       (0, 0, 128)]),
+                                         dict(N=1 << 22, strides=[(0, 0, 128), (0, 0, 1024),
+                                                                  (0, 0, 128), (0, 0, 128)])],
+                         ids=lambda b: ",".join(b))
+def test_attn_unsupported(L, unsupported):
+    assert _attn(L, **unsupported) == hk.HK_ERROR_NOT_SUPPORTED
+
+
+def test_attn_empty_is_a_noop_success(L):
+    assert _attn(L, B=0, Q=0, K=0, V=0, O=0) == hk.HK_SUCCESS
+    assert _attn(L, N=0, Q=0, K=0, V=0, O=0) == hk.HK_SUCCESS
+    assert _attn(L, Hq=0, Q=0, K=0, V=0, O=0) == hk.HK_SUCCESS
