@@ -30,6 +30,10 @@
 //
 // Two workgroups share a compute unit (2 waves per SIMD), so one wave's
 // softmax arithmetic runs while the other's matrix instructions do.
+//
+// The softmax reference point moves lazily: only when a query's block max
+// exceeds it by more than kLazy (log2 units) is the output rescaled, so most
+// blocks skip the rescale; the weights then stay below 2^kLazy.
 #pragma once
 
 #include "hk_device.hpp"
@@ -52,6 +56,7 @@ struct AttnArgs {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnQ = 128;   // query rows per workgroup
 constexpr int kAttnKV = 64;   // keys per block
+constexpr float kLazy = 8.0f; // log2 headroom before the softmax reference moves
 
 // LDS image of one block of K or V: 64 rows (keys) x D bf16, 16-byte chunk c
 // of row r at physical chunk c ^ key(r).
@@ -193,15 +198,15 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
     float m[2] = {-INFINITY, -INFINITY};  // running max of S * c (log2 units)
     float l[2] = {0.f, 0.f};              // this lane's share of the running sum
 
+    // One barrier per block: past it, block j has landed (every wave waited
+    // for its own part) and every wave has finished block j - 1, whose
+    // buffer then takes block j + 1.
     if (nblk > 0) issue(0);
     for (int32_t j = 0; j < nblk; ++j) {
-        if (j + 1 < nblk) {
-            issue(j + 1);
-            wait_vmcnt<2 * kLoads>();  // block j has landed (this wave's part)
-        } else {
-            wait_vmcnt0();
-        }
-        fenced_barrier();  // ... and every wave's part
+        wait_vmcnt0();
+        wait_lgkmcnt0();
+        fenced_barrier();
+        if (j + 1 < nblk) issue(j + 1);
         const HK_LDS uint8_t* kimg = lds + (uint32_t)(j & 1) * 2u * kImgB;
         const HK_LDS uint8_t* vimg = kimg + kImgB;
         const int32_t k0 = j * kAttnKV;
@@ -243,18 +248,28 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
                 for (int e = 1; e < 16; ++e) mx = fmaxf(mx, t[e]);
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mnew = fmaxf(m[qb], mx);
-                const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
-                m[qb] = mnew;
+                // The reference point m moves only when some query of the
+                // wave gains more than kLazy over it: until then the weights
+                // stay below 2^kLazy, and O and l carry the same stale
+                // factor, which the final O / l cancels.
+                if (__builtin_amdgcn_ballot_w64(mx > m[qb] + kLazy) != 0) {
+                    const float mnew = fmaxf(m[qb], mx);
+                    // (a query with no visible key yet keeps m = -inf)
+                    const float alpha =
+                        mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[qb] - mnew);
+                    m[qb] = mnew;
+                    l[qb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < kDB; ++db) o[db][qb] *= alpha;
+                }
+                const float mref = m[qb];
                 float p[16], sum = 0.f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    p[e] = __builtin_amdgcn_exp2f(t[e] - mnew);
+                    p[e] = __builtin_amdgcn_exp2f(t[e] - mref);
                     sum += p[e];
                 }
-                l[qb] = l[qb] * alpha + sum;
-#pragma unroll
-                for (int db = 0; db < kDB; ++db) o[db][qb] *= alpha;
+                l[qb] += sum;
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const float* pc = p + 8 * c;
@@ -272,8 +287,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
                     o[db][1] = mfma_bf16_16x16x32(vf, pf[1][c], o[db][1]);
                 }
         }
-        wait_lgkmcnt0();
-        fenced_barrier();  // every wave is done with this buffer
     }
 
     // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
