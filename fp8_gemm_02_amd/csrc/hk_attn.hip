@@ -36,7 +36,7 @@ extern "C" hk_status hk_attn_fwd_bf16(const void* Q, const void* K, const void* 
                                       float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                       int64_t D, float scale, int32_t causal,
                                       const hk_attn_strides* strides, hk_stream_t stream) {
-    if (B < 0 || Hq < 0 || N < 0 || Hkv < 1 || D < 1 || Hq % Hkv != 0 || !isfinite(scale))
+    if (B < 0 || Hq < 0 || N < 0 || Hkv < 1 || D < 1 || Hq % Hkv != 0 || !(isfinite(scale) && scale > 0.0f))
         return HK_ERROR_INVALID_VALUE;
     hk_attn_strides st;
     if (strides) {

@@ -74,6 +74,22 @@ __device__ __forceinline__ uint32_t attn_vswz(uint32_t r) {
     return D == 128 ? 2u * (r & 7u) : 2u * ((r >> 1) & 3u);
 }
 
+// max of x over the four lanes l, l^16, l^32, l^48 (the lanes that share a
+// query): lane l^16 through ds_swizzle (bit mode: and 0x1F, xor 0x10, within
+// 32 lanes), lane l^32 through ds_bpermute (byte address x32 = 4 (l ^ 32)).
+__device__ __forceinline__ float max_across_groups(float x, int32_t x32) {
+    const int u = __builtin_bit_cast(int, x);
+    const float y = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(u, 0x401F)));
+    const int v = __builtin_bit_cast(int, y);
+    return fmaxf(y, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, v)));
+}
+__device__ __forceinline__ float sum_across_groups(float x, int32_t x32) {
+    const int u = __builtin_bit_cast(int, x);
+    const float y = x + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(u, 0x401F));
+    const int v = __builtin_bit_cast(int, y);
+    return y + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, v));
+}
+
 // workgroup -> (batch * Hq + head, query block).  Workgroups are dealt to
 // the 8 chiplets round-robin; when the count allows, each chiplet gets a
 // contiguous range of heads, so that a head's K and V stay in one L2.
@@ -91,6 +107,7 @@ template <int D, bool kCausal>
 __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t* lds) {
     constexpr int kDC = D / 32;                    // 32-wide d chunks (S MFMAs)
     constexpr int kDB = D / 16;                    // 16-wide d blocks (O MFMAs)
+    constexpr int kVPre = kDB / 2;                 // V d blocks read before the softmax
     constexpr uint32_t kRowB = D * 2;              // bytes per K/V row
     constexpr uint32_t kImgB = kAttnKV * kRowB;    // bytes per K or V block image
     constexpr uint32_t kRowsPerLoad = 1024u / kRowB;
@@ -195,8 +212,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-INFINITY, -INFINITY};  // running max of S * c (log2 units)
-    float l[2] = {0.f, 0.f};              // this lane's share of the running sum
+    float m[2] = {-INFINITY, -INFINITY};  // softmax reference per query (log2 units)
+    float l[2] = {0.f, 0.f};              // this lane's share of the sum of weights
+    const int32_t x32 = (int32_t)((lane ^ 32u) << 2);
 
     // One barrier per block: past it, block j has landed (every wave waited
     // for its own part) and every wave has finished block j - 1, whose
@@ -213,41 +231,66 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
 
         // a wave whose queries all lie before this block has nothing to add
         if (!kCausal || k0 <= q0w + 31) {
+            // Phases, each fenced from the next so that the reads of a phase
+            // are all in flight before its first consumer waits: K reads;
+            // S MFMAs; the V reads of the first kVPre d blocks (landing
+            // during the softmax); softmax; the other V reads; O MFMAs.
             // ---- S^T = K Q^T
+            i32x4 kf[4][kDC];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int dc = 0; dc < kDC; ++dc) kf[kb][dc] = read_k(kimg, kb, dc);
+            __builtin_amdgcn_sched_barrier(0);
             f32x4 s[4][2];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int dc = 0; dc < kDC; ++dc) {
-                    const i32x4 kf = read_k(kimg, kb, dc);
-                    s[kb][0] = mfma_bf16_16x16x32(kf, qf[0][dc], s[kb][0]);
-                    s[kb][1] = mfma_bf16_16x16x32(kf, qf[1][dc], s[kb][1]);
+                    s[kb][0] = mfma_bf16_16x16x32(kf[kb][dc], qf[0][dc], s[kb][0]);
+                    s[kb][1] = mfma_bf16_16x16x32(kf[kb][dc], qf[1][dc], s[kb][1]);
                 }
             }
-            // ---- online softmax, per query (lane l%16) in log2 units
+            // ---- masked scores (causal, or keys past N) become -inf, on a
+            // separate path that blocks away from the edges skip
             const bool masked = (kCausal && k0 + kAttnKV - 1 > q0w) || k0 + kAttnKV > N;
+            if (masked) {
+                // key = k0 + 16kb + 4(l/16) + v and q = q0w + 16qb + l%16:
+                // compare the lane's constant part against a scalar threshold
+                const int32_t dq = 4 * (int32_t)g4 - (int32_t)r16;
+                const int32_t g4x4 = 4 * (int32_t)g4;
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const bool after_q = dq > q0w - k0 + 16 * (qb - kb) - v;  // key > q
+                            const bool past_n = g4x4 >= N - k0 - 16 * kb - v;         // key >= N
+                            if ((kCausal && after_q) || past_n) s[kb][qb][v] = -INFINITY;
+                        }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            i32x4 vf[kDB][2];
+#pragma unroll
+            for (int db = 0; db < kVPre; ++db)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) vf[db][c] = read_vt(vimg, db, c);
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- online softmax, per query (lane l%16) in log2 units.  With
+            // c = scale * log2(e) > 0, max_j (c s_j) = c max_j s_j, and each
+            // weight is exp2(c s_j - m): one fma and one exp2 per score.
             i32x4 pf[2][2];  // P^T fragments: [qb][c]
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                const int32_t q = q0w + 16 * qb + (int32_t)r16;
-                float t[16];
+                float mx = s[0][qb][0];
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        float x = s[kb][qb][v] * g.c;
-                        if (masked) {
-                            const int32_t key = k0 + 16 * kb + 4 * (int32_t)g4 + v;
-                            if ((kCausal && key > q) || key >= N) x = -INFINITY;
-                        }
-                        t[4 * kb + v] = x;
-                    }
-                float mx = t[0];
-#pragma unroll
-                for (int e = 1; e < 16; ++e) mx = fmaxf(mx, t[e]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][qb][v]);
+                mx = max_across_groups(mx, x32);
+                mx *= g.c;
                 // The reference point m moves only when some query of the
                 // wave gains more than kLazy over it: until then the weights
                 // stay below 2^kLazy, and O and l carry the same stale
@@ -262,29 +305,33 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
 #pragma unroll
                     for (int db = 0; db < kDB; ++db) o[db][qb] *= alpha;
                 }
-                const float mref = m[qb];
-                float p[16], sum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    p[e] = __builtin_amdgcn_exp2f(t[e] - mref);
-                    sum += p[e];
-                }
-                l[qb] += sum;
+                const float nm = -m[qb];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    const float* pc = p + 8 * c;
-                    pf[qb][c] = i32x4{(int)pack_bf16x2(pc[0], pc[1]), (int)pack_bf16x2(pc[2], pc[3]),
-                                      (int)pack_bf16x2(pc[4], pc[5]), (int)pack_bf16x2(pc[6], pc[7])};
+                    float p[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        p[e] = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(s[2 * c + e / 4][qb][e % 4], g.c, nm));
+                    // the sum takes the fp32 weights, so that LSE is exact to
+                    // fp32 sums; O carries the bf16 ones
+                    l[qb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+                    pf[qb][c] = i32x4{(int)pack_bf16x2(p[0], p[1]), (int)pack_bf16x2(p[2], p[3]),
+                                      (int)pack_bf16x2(p[4], p[5]), (int)pack_bf16x2(p[6], p[7])};
                 }
             }
             // ---- O^T += V^T P^T
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = kVPre; db < kDB; ++db)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) vf[db][c] = read_vt(vimg, db, c);
 #pragma unroll
             for (int db = 0; db < kDB; ++db)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    const i32x4 vf = read_vt(vimg, db, c);
-                    o[db][0] = mfma_bf16_16x16x32(vf, pf[0][c], o[db][0]);
-                    o[db][1] = mfma_bf16_16x16x32(vf, pf[1][c], o[db][1]);
+                    o[db][0] = mfma_bf16_16x16x32(vf[db][c], pf[0][c], o[db][0]);
+                    o[db][1] = mfma_bf16_16x16x32(vf[db][c], pf[1][c], o[db][1]);
                 }
         }
     }
@@ -293,9 +340,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
     uint16_t* Oh = g.O + (int64_t)b * g.so[0] + (int64_t)h * g.so[1];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        float lt = l[qb];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = sum_across_groups(l[qb], x32);
         const int32_t q = q0w + 16 * qb + (int32_t)r16;
         if (q < N) {
             const float inv = 1.0f / lt;

@@ -28,9 +28,9 @@
  * Device pointers owned by the caller; one kernel enqueued on `stream`; no
  * allocation, no synchronisation.  HK_ERROR_INVALID_VALUE, before any HIP
  * call: negative B, Hq, Hkv or N; Hkv < 1 or Hq not a multiple of Hkv;
- * D < 1; a non-finite scale; a NULL Q, K, V or O when there is work; a
- * negative stride or a token stride below D.  HK_ERROR_NOT_SUPPORTED: D other
- * than 64 or 128; Q, K, V or O not 16-byte aligned; a stride not a multiple
+ * D < 1; a scale that is not finite and positive; a NULL Q, K, V or O when
+ * there is work; a negative stride or a token stride below D.
+ * HK_ERROR_NOT_SUPPORTED: D other than 64 or 128; Q, K, V or O not 16-byte aligned; a stride not a multiple
  * of 8; (N + 128) token strides of K or V spanning 2^31 bytes or more.
  * B * Hq * N == 0 is a no-op success.
  */

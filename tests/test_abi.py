@@ -380,6 +380,7 @@ def _attn(L, **kw):
 
 @pytest.mark.parametrize("bad", [dict(B=-1), dict(Hq=-1), dict(N=-1), dict(Hkv=0), dict(Hq=3),
                                  dict(D=0), dict(scale=float("nan")), dict(scale=float("inf")),
+                                 dict(scale=0.0), dict(scale=-0.5),
                                  dict(Q=0), dict(K=0), dict(V=0), dict(O=0),
                                  dict(strides=[(0, 0, 127), (0, 0, 128), (0, 0, 128), (0, 0, 128)]),
                                  dict(strides=[(-8, 0, 128), (0, 0, 128), (0, 0, 128), (0, 0, 128)])],
