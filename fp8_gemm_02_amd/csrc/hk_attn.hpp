@@ -77,11 +77,20 @@ __device__ __forceinline__ uint32_t attn_vswz(uint32_t r) {
 // max of x over the four lanes l, l^16, l^32, l^48 (the lanes that share a
 // query): lane l^16 through ds_swizzle (bit mode: and 0x1F, xor 0x10, within
 // 32 lanes), lane l^32 through ds_bpermute (byte address x32 = 4 (l ^ 32)).
-__device__ __forceinline__ float max_across_groups(float x, int32_t x32) {
-    const int u = __builtin_bit_cast(int, x);
-    const float y = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(u, 0x401F)));
-    const int v = __builtin_bit_cast(int, y);
-    return fmaxf(y, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, v)));
+//
+// In the block loop the max goes through v_permlane16_swap / v_permlane32_swap
+// instead, which stay off the LDS pipe: swapping a register with a copy of
+// itself leaves in the pair, per lane, its own value and its partner's (rows
+// of 16 lanes swapped pairwise, or the two halves), and max is symmetric in
+// the pair.  Issued as assembly (the compiler folded away one half of the
+// pair of the builtin), with the two wait states a VALU write needs before a
+// permlane reads it.
+__device__ __forceinline__ float max_across_groups(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    float c = fmaxf(a, b), d = c;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+    return fmaxf(c, d);
 }
 __device__ __forceinline__ float sum_across_groups(float x, int32_t x32) {
     const int u = __builtin_bit_cast(int, x);
@@ -289,7 +298,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][qb][v]);
-                mx = max_across_groups(mx, x32);
+                mx = max_across_groups(mx);
                 mx *= g.c;
                 // The reference point m moves only when some query of the
                 // wave gains more than kLazy over it: until then the weights
