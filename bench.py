@@ -308,8 +308,8 @@ def cpu_baseline_attn(w, x, seconds: float):
         keys = (rows % w.N + 1) if w.causal else np.full(n, w.N)
         return t, 4.0 * w.D * float(keys.sum())
 
-    t, _ = run(threads)
-    n = int(max(threads, min(nrow, seconds / max(t / threads, 1e-9))))
+    t, _ = run(8 * threads)  # calibration sample, large enough to amortise start-up
+    n = int(max(threads, min(nrow, seconds / max(t / (8 * threads), 1e-9))))
     t, flops = run(n)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model(),
