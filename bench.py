@@ -44,6 +44,9 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the per-launch timing after an L2/LLC flush")
+    ap.add_argument("--library-context", action="store_true",
+                    help="also time torch's own GEMM (hipBLASLt: torch.matmul for BF16, "
+                         "torch._scaled_mm for FP8) on the same stored operands, as context")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="instead of the GEMM, run one plain device-to-device copy of BYTES "
                          "bytes (torch copy_) 5 times; the HBM byte counters read on it "
@@ -128,6 +131,53 @@ def cpu_baseline(w, x, seconds: float):
             "cpu_model": cpu_model(),
             "sample": "%d of %d output rows (all %d columns, K=%d), FP64 scalar oracle, %.1f s"
                       % (rows, w.M, w.N, w.K, t)}
+
+
+def library_context(a, w, A, B, sa, sb, stream):
+    """torch's own GEMM on the same stored operands, timed like the main launches.
+
+    Context only: the library is hipBLASLt (torch.matmul for BF16,
+    torch._scaled_mm with per-tensor scales for FP8).  The logical M x K and
+    N x K operands are views of the stored arrays, so a K-strided layout
+    reaches the library as a transposed view.
+    """
+    import torch
+    if w.dtype == "mxfp8":
+        return None
+    Al = A if not w.layout_a else A.t()
+    Bl = B if not w.layout_b else B.t()
+    out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=A.device)
+    if w.dtype == "bf16":
+        name = "torch.matmul (hipBLASLt)"
+
+        def lib_step():
+            torch.matmul(Al, Bl.t(), out=out)
+    else:
+        name = "torch._scaled_mm (hipBLASLt)"
+        Al = Al.view(torch.float8_e4m3fn)  # the stored E4M3 bytes
+        Bl = Bl.view(torch.float8_e4m3fn)
+        ta = torch.tensor(sa, dtype=torch.float32, device=A.device)
+        tb = torch.tensor(sb, dtype=torch.float32, device=A.device)
+
+        def lib_step():
+            torch._scaled_mm(Al, Bl.t(), scale_a=ta, scale_b=tb, out_dtype=torch.bfloat16,
+                             out=out)
+    with torch.cuda.stream(stream):
+        for _ in range(a.warmup):
+            lib_step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    with torch.cuda.stream(stream):
+        for i in range(a.steps):
+            starts[i].record(stream)
+            lib_step()
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
+    mean_ms = sum(durs) / len(durs)
+    return {"library": name, "tflops": round(w.flops / (mean_ms * 1e-3) / 1e12, 2),
+            "kernel_ms": {"mean": round(mean_ms, 4), "median": round(durs[len(durs) // 2], 4)}}
 
 
 def cpu_model() -> str:
@@ -262,6 +312,9 @@ def main():
                             "arithmetic_intensity": round(ai, 1), "ridge": round(ridge, 1),
                             "algorithmic_flops_per_launch": flops,
                             "algorithmic_bytes_per_launch": w.algorithmic_bytes})
+
+    if a.library_context:
+        out["library_context"] = library_context(a, w, A, B, sa, sb, stream)
 
     if not a.no_flush:
         # per-launch time after flushing L2 and the last-level cache (a 1 GiB
