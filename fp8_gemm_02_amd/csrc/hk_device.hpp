@@ -187,13 +187,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// Store four consecutive bf16 of one C row starting at column n, touching
-// only columns < N.  align is the guaranteed byte alignment of every
-// 4-column group start (8, 4 or 2).
-__device__ __forceinline__ void store_bf16x4(uint16_t* p, int32_t n, int32_t N, f32x4 v,
-                                             int32_t align) {
-    const uint32_t lo = pack_bf16x2(v.x, v.y);
-    const uint32_t hi = pack_bf16x2(v.z, v.w);
+// Store four consecutive bf16 of one C row, packed in two dwords (lo holds
+// columns n, n+1), starting at column n and touching only columns < N.
+// align is the guaranteed byte alignment of every 4-column group start
+// (16, 8, 4 or 2).
+__device__ __forceinline__ void store_packed4(uint16_t* p, int32_t n, int32_t N, uint32_t lo,
+                                              uint32_t hi, int32_t align) {
     if (n + 4 <= N) {
         if (align >= 8) {
             *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
@@ -210,6 +209,73 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, int32_t n, int32_t N, 
         if (n + 0 < N) p[0] = (uint16_t)lo;
         if (n + 1 < N) p[1] = (uint16_t)(lo >> 16);
         if (n + 2 < N) p[2] = (uint16_t)hi;
+    }
+}
+
+// The same from four fp32 values (rounded to nearest even).
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, int32_t n, int32_t N, f32x4 v,
+                                             int32_t align) {
+    store_packed4(p, n, N, pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w), align);
+}
+
+// The lane's index in its wave, computed where it is called: as a volatile
+// statement it is not hoisted out of a loop, so nothing holds it live across
+// one (the 4-wave kernels use all 256 VGPRs there).
+__device__ __forceinline__ uint32_t lane_id_here() {
+    uint32_t l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// Swap between lane groups: rows of 16 lanes pair up as (0, 1) and (2, 3);
+// the odd rows of x trade places with the even rows of y.  Afterwards a lane
+// of an even row holds its own x and its partner's x in y; a lane of an odd
+// row holds its partner's y in x and its own y.  The s_nop gives the two
+// wait states a VALU write needs before the permute reads it.
+__device__ __forceinline__ void swap_row_pairs(uint32_t& x, uint32_t& y) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(x), "+v"(y));
+}
+
+// Store one 16-row block of a wave's C sub-tile.  Lane (r, g) (r = lane % 16,
+// g = lane / 16) holds, for blocks j = 0..7, C[m][c0 + 16j + 4g .. +3] in
+// a[j] (times s); m is the lane's row, ok whether it lies inside C.  With
+// 16-byte aligned 8-column groups (align 16) each pair of blocks (j, j+1)
+// goes out as one 16-byte store per lane: lane groups g and g+1 trade their
+// halves (swap_row_pairs), so that even groups hold columns
+// c0 + 16j + 4g .. +7 and odd groups c0 + 16(j+1) + 4(g-1) .. +7.  Half the
+// store instructions of 8-byte stores, each covering 64 bytes of a row.
+__device__ __forceinline__ void store_c_rows(uint16_t* crow, bool ok, int32_t c0, uint32_t g,
+                                             int32_t N, const f32x4 (&a)[8], float s,
+                                             int32_t align) {
+    // an opaque copy of the lane group: the column offsets below are then
+    // computed here, not hoisted out of the tile loop and kept live (spilled)
+    // across it
+    asm volatile("" : "+v"(g));
+    if (align >= 16) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            const f32x4 u = a[j] * s, v = a[j + 1] * s;
+            uint32_t x0 = pack_bf16x2(u.x, u.y), x1 = pack_bf16x2(u.z, u.w);
+            uint32_t y0 = pack_bf16x2(v.x, v.y), y1 = pack_bf16x2(v.z, v.w);
+            swap_row_pairs(x0, y0);
+            swap_row_pairs(x1, y1);
+            const int32_t c = c0 + ((g & 1u) ? 16 * (j + 1) + 4 * (int32_t)(g - 1)
+                                             : 16 * j + 4 * (int32_t)g);
+            if (ok) {
+                if (c + 8 <= N) {
+                    *reinterpret_cast<uint4*>(crow + c) = make_uint4(x0, x1, y0, y1);
+                } else {
+                    store_packed4(crow + c, c, N, x0, x1, align);
+                    store_packed4(crow + c + 4, c + 4, N, y0, y1, align);
+                }
+            }
+        }
+    } else if (ok) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int32_t n = c0 + 16 * j + 4 * (int32_t)g;
+            if (n < N) store_bf16x4(crow + n, n, N, a[j] * s, align);
+        }
     }
 }
 

@@ -347,7 +347,10 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     g.ldsa = g.ldsb = 0;
     g.a_t = at;
     g.b_t = bt;
-    g.c_align = (aligned(C, 8) && ldc % 4 == 0) ? 8 : (aligned(C, 4) && ldc % 2 == 0) ? 4 : 2;
+    g.c_align = (aligned(C, 16) && ldc % 8 == 0) ? 16
+                : (aligned(C, 8) && ldc % 4 == 0)  ? 8
+                : (aligned(C, 4) && ldc % 2 == 0)  ? 4
+                                                   : 2;
     g.grid.order = order == HK_GRID_ROW_MAJOR ? hk::kGridRowMajor : hk::kGridXcd;
     g.grid.tiles_m = (int32_t)p->tiles_m;
     g.grid.tiles_n = (int32_t)p->tiles_n;

@@ -43,7 +43,7 @@ struct GemmArgs {
     uint32_t lda_b, ldb_b;  // row strides of A and B in bytes
     int64_t ldc;            // row stride of C in elements
     float scale;            // multiplies the fp32 accumulator (FP8 only)
-    int32_t c_align;        // guaranteed alignment of 4-column groups of C: 8, 4 or 2
+    int32_t c_align;        // guaranteed alignment of 8-column (16) or 4-column groups of C (8, 4, 2)
     GridParams grid;
     // MXFP8 only: E8M0 scale bytes, one per 32 K-elements of a row
     const uint8_t* SA;
@@ -578,19 +578,13 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         acc_settle();  // the last MFMA results before the epilogue reads them
 
         // ---- epilogue: lane holds C[m][n..n+3] for each (mb, nb)
-        const int32_t mrow = cur.m0 + (int32_t)(arow + r16);
-        const int32_t ncol = cur.n0 + (int32_t)(brow + g4 * 4u);
+        const uint32_t le = lane_id_here();
+        const int32_t mrow = cur.m0 + (int32_t)(arow + (le & 15u));
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const int32_t m = mrow + mb * 16;
-            if (m < g.M) {
-                uint16_t* crow = g.C + (int64_t)m * g.ldc;
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) {
-                    const int32_t n = ncol + nb * 16;
-                    if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb], g.c_align);
-                }
-            }
+            store_c_rows(g.C + (int64_t)m * g.ldc, m < g.M, cur.n0 + (int32_t)brow, le >> 4, g.N,
+                         acc[mb], 1.0f, g.c_align);
         }
         if (w_next >= total) break;
         w = w_next;
@@ -869,18 +863,11 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
 
         // ---- epilogue: lane holds C[m][n..n+3] of block (mb, nb), times sA*sB
         const int32_t mrow = cur.m0 + (int32_t)(arow + r16);
-        const int32_t ncol = cur.n0 + (int32_t)(brow + g4 * 4u);
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const int32_t m = mrow + mb * 16;
-            if (m < g.M) {
-                uint16_t* crow = g.C + (int64_t)m * g.ldc;
-#pragma unroll
-                for (int nb = 0; nb < 8; ++nb) {
-                    const int32_t n = ncol + nb * 16;
-                    if (n < g.N) store_bf16x4(crow + n, n, g.N, acc[mb][nb] * g.scale, g.c_align);
-                }
-            }
+            store_c_rows(g.C + (int64_t)m * g.ldc, m < g.M, cur.n0 + (int32_t)brow, g4, g.N,
+                         acc[mb], g.scale, g.c_align);
         }
         if (w_next >= total) break;
         w = w_next;

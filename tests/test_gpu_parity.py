@@ -227,6 +227,39 @@ def test_odd_ldc_two_byte_stores():
     assert oracle.compare(allb[:, :N], ref, exact=True)["ok"]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 7, 8, 9, 12, 260, 263, 264, 268, 516])
+def test_sixteen_byte_stores_and_ragged_columns(dtype, N):
+    """C 16-byte aligned with ldc a multiple of 8: the 4-wave kernels store
+    8 columns per lane after trading halves between lane groups; a group that
+    crosses N is stored column by column.  Bit-exact, padding and guard rows
+    untouched."""
+    M, K = 300, 192
+    ldc = (N + 7) // 8 * 8 + 8
+    if dtype == "bf16":
+        A, B, sa, sb = _bf16(M, K, "int4", 71), _bf16(N, K, "int4", 72), 1.0, 1.0
+        dt = hk.HK_DTYPE_BF16
+    else:
+        A, _ = gemm_inputs.fp8_matrix(M, K, 73, integer=True)
+        B, _ = gemm_inputs.fp8_matrix(N, K, 74, integer=True)
+        sa, sb, dt = 0.5, 4.0, hk.HK_DTYPE_FP8_E4M3
+    guard = 2
+    Cbuf = torch.full(((M + 2 * guard) * ldc,), SENTINEL, dtype=torch.int16,
+                      device="cuda").view(torch.bfloat16)
+    Cv = Cbuf[guard * ldc:]
+    assert Cv.data_ptr() % 16 == 0 and ldc % 8 == 0
+    _say("16-byte stores", dtype, (M, N, K), "ldc", ldc)
+    _run(dt, A.cuda(), B.cuda(), M, N, K, K, K, ldc, sa, sb, C=Cv, schedule="interleave4")
+    allb = _bits16(Cbuf).reshape(M + 2 * guard, ldc)
+    assert (allb[:guard] == SENTINEL).all() and (allb[guard + M:] == SENTINEL).all()
+    body = allb[guard:guard + M]
+    assert (body[:, N:] == SENTINEL).all()
+    ref, _ = oracle.gemm(dtype, gemm_inputs.bits(A).ravel(), gemm_inputs.bits(B).ravel(), M, N, K,
+                         scale_a=sa, scale_b=sb)
+    st = oracle.compare(body[:, :N], ref, exact=True)
+    assert st["ok"], st
+
+
 def test_zero_k_writes_zeros_and_empty_is_noop():
     C = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
     hk.hk_gemm_bf16(0, 0, C, 5, 7, 0, 1, 1, 7)
