@@ -363,6 +363,25 @@ __device__ __forceinline__ uint32_t km_key(uint32_t k) {
 constexpr uint32_t kKMRowBytes = kIL4Tile * 2u;    // one K-row of a transposed stage image
 constexpr uint32_t kKMStageRows = kRowBytes / 2u;  // 64 K-rows of bf16 per stage
 
+// Chiplet-rotated K order of the persistent 4-wave kernels.  All CUs walk
+// the K stages of their tiles in lockstep, and the 8 chiplets share each
+// A (or B) panel of a window: with one K order, all 8 L2s miss on the same
+// lines at the same moment and queue at the last-level cache (fabric read
+// latency about 1.5 times hipBLASLt's, measured with TCC_EA0_RDREQ_LEVEL).
+// Chiplet x (workgroup w runs on chiplet w mod 8) starts its tiles' whole
+// stages x/8 of the way into K and wraps around; the CUs of one chiplet keep
+// one order, so their L2 sharing is untouched.  The partial last stage and
+// the stages past K keep their places.  Only the order of the fp32 sums
+// changes.
+__device__ __forceinline__ uint32_t chiplet_k_rotation(uint32_t nk_whole) {
+    return ((blockIdx.x & 7u) * nk_whole) >> 3;
+}
+__device__ __forceinline__ uint32_t rotated_stage(uint32_t s, uint32_t rot, uint32_t nk_whole) {
+    if (s >= nk_whole) return s;
+    const uint32_t r = s + rot;
+    return r >= nk_whole ? r - nk_whole : r;
+}
+
 template <bool kAT, bool kBT>
 __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf buf0,
                                               const IL4Buf buf1) {
@@ -422,7 +441,9 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     // tile tt into buffer d.  Masked: lanes whose chunk lies at or past K
     // (every lane, for a stage past the end) read zeros; the main loop, whose
     // stages all lie inside K, skips that select.
-    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s, int i) {
+    const uint32_t krot = chiplet_k_rotation(nk_whole);
+    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i) {
+        const uint32_t s = rotated_stage(s0, krot, nk_whole);
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
         const bool km = i < 8 ? kAT : kBT;
@@ -712,7 +733,9 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         if constexpr (decltype(masked)::value) v = 4u * s + (lane >> 4) < nblocks ? v : 127u;
         return v;
     };
-    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s, int i) {
+    const uint32_t krot = kMx ? 0u : chiplet_k_rotation(nk_whole);
+    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i) {
+        const uint32_t s = rotated_stage(s0, krot, nk_whole);
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
         uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
