@@ -133,17 +133,16 @@ def cpu_baseline(w, x, seconds: float):
                       % (rows, w.M, w.N, w.K, t)}
 
 
-def library_context(a, w, A, B, sa, sb, stream):
+def library_context(a, w, A, B, sa, sb, stream, SA=None, SB=None):
     """torch's own GEMM on the same stored operands, timed like the main launches.
 
     Context only: the library is hipBLASLt (torch.matmul for BF16,
-    torch._scaled_mm with per-tensor scales for FP8).  The logical M x K and
-    N x K operands are views of the stored arrays, so a K-strided layout
-    reaches the library as a transposed view.
+    torch._scaled_mm with per-tensor scales for FP8, and with 1 x 32 E8M0
+    block scales, given as the same M x K/32 and N x K/32 byte matrices, for
+    MXFP8).  The logical M x K and N x K operands are views of the stored
+    arrays, so a K-strided layout reaches the library as a transposed view.
     """
     import torch
-    if w.dtype == "mxfp8":
-        return None
     Al = A if not w.layout_a else A.t()
     Bl = B if not w.layout_b else B.t()
     out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=A.device)
@@ -156,8 +155,13 @@ def library_context(a, w, A, B, sa, sb, stream):
         name = "torch._scaled_mm (hipBLASLt)"
         Al = Al.view(torch.float8_e4m3fn)  # the stored E4M3 bytes
         Bl = Bl.view(torch.float8_e4m3fn)
-        ta = torch.tensor(sa, dtype=torch.float32, device=A.device)
-        tb = torch.tensor(sb, dtype=torch.float32, device=A.device)
+        if w.dtype == "mxfp8":
+            name = "torch._scaled_mm, 1 x 32 E8M0 block scales (hipBLASLt)"
+            ta = SA.view(torch.float8_e8m0fnu)
+            tb = SB.view(torch.float8_e8m0fnu)
+        else:
+            ta = torch.tensor(sa, dtype=torch.float32, device=A.device)
+            tb = torch.tensor(sb, dtype=torch.float32, device=A.device)
 
         def lib_step():
             torch._scaled_mm(Al, Bl.t(), scale_a=ta, scale_b=tb, out_dtype=torch.bfloat16,
@@ -314,7 +318,8 @@ def main():
                             "algorithmic_bytes_per_launch": w.algorithmic_bytes})
 
     if a.library_context:
-        out["library_context"] = library_context(a, w, A, B, sa, sb, stream)
+        out["library_context"] = library_context(a, w, A, B, sa, sb, stream,
+                                                 *((SA, SB) if w.dtype == "mxfp8" else ()))
 
     if not a.no_flush:
         # per-launch time after flushing L2 and the last-level cache (a 1 GiB
