@@ -260,6 +260,32 @@ def test_sixteen_byte_stores_and_ragged_columns(dtype, N):
     assert st["ok"], st
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_k_order_does_not_change_exact_results(dtype):
+    """The 4-wave kernels walk K in a per-chiplet rotated order (chiplet
+    w mod 8 starts w mod 8 eighths of the way in).  Changing the tile order
+    moves tiles to other chiplets and so changes their K order: on
+    integer-valued inputs every order must give the oracle's bits.  K has a
+    tail and a whole-stage count that is not a multiple of 8."""
+    M, N, K = 1100, 700, 1000 if dtype == "bf16" else 1936
+    if dtype == "bf16":
+        A, B, sa, sb = _bf16(M, K, "int4", 81), _bf16(N, K, "int4", 82), 1.0, 1.0
+        dt = hk.HK_DTYPE_BF16
+    else:
+        A, _ = gemm_inputs.fp8_matrix(M, K, 83, integer=True)
+        B, _ = gemm_inputs.fp8_matrix(N, K, 84, integer=True)
+        sa, sb, dt = 0.5, 4.0, hk.HK_DTYPE_FP8_E4M3
+    ref, _ = oracle.gemm(dtype, gemm_inputs.bits(A).ravel(), gemm_inputs.bits(B).ravel(), M, N, K,
+                         scale_a=sa, scale_b=sb)
+    Ad, Bd = A.cuda(), B.cuda()
+    for opts in (dict(grid_order="xcd"), dict(grid_order="row_major"),
+                 dict(grid_order="xcd", group_m=1), dict(grid_order="xcd", window=24)):
+        _say("K order", dtype, (M, N, K), opts)
+        C = _run(dt, Ad, Bd, M, N, K, K, K, N, sa, sb, schedule="interleave4", **opts)
+        st = oracle.compare(_bits16(C), ref, exact=True)
+        assert st["ok"], (opts, st)
+
+
 def test_zero_k_writes_zeros_and_empty_is_noop():
     C = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
     hk.hk_gemm_bf16(0, 0, C, 5, 7, 0, 1, 1, 7)
