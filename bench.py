@@ -197,8 +197,9 @@ def cpu_model() -> str:
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU only; --gpus %d is not supported (every box here has "
-              "a single MI355X, and this GEMM has no multi-GPU path)" % a.gpus, file=sys.stderr)
+        print("bench.py measures one GPU only; --gpus %d is not supported: this GEMM has no "
+              "multi-GPU path (an M or N split needs no exchange: run one process per GPU on its "
+              "share of the output)" % a.gpus, file=sys.stderr)
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration(a.copy_calibration)
