@@ -166,6 +166,12 @@ def library_context(a, w, A, B, sa, sb, stream, SA=None, SB=None):
         def lib_step():
             torch._scaled_mm(Al, Bl.t(), scale_a=ta, scale_b=tb, out_dtype=torch.bfloat16,
                              out=out)
+    try:
+        with torch.cuda.stream(stream):
+            lib_step()
+        torch.cuda.synchronize()
+    except RuntimeError as e:  # a storage the library does not take
+        return {"library": name, "unsupported": str(e).splitlines()[0][:200]}
     with torch.cuda.stream(stream):
         for _ in range(a.warmup):
             lib_step()

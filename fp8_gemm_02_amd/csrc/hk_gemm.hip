@@ -75,6 +75,25 @@ hk_gemm_il4_fp8(hk::GemmArgs g) {
     hk::il4_fp8_body<false>(g, buf0, buf1, nullptr);
 }
 
+// FP8 operands stored K-strided: A as K x M ("akm"), B as K x N ("bkn")
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_fp8_akm(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_fp8_body<false, true, false>(g, buf0, buf1, nullptr);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_fp8_bkn(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_fp8_body<false, false, true>(g, buf0, buf1, nullptr);
+}
+
+extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
+hk_gemm_il4_fp8_akm_bkn(hk::GemmArgs g) {
+    HK_IL4_LDS;
+    hk::il4_fp8_body<false, true, true>(g, buf0, buf1, nullptr);
+}
+
 // MXFP8: the FP8 4-wave kernel plus two 8 KiB buffers of block scales (144 KiB).
 extern "C" __global__ void __launch_bounds__(hk::kIL4Threads)
 hk_gemm_il4_mxfp8(hk::GemmArgs g) {
@@ -227,17 +246,19 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     const int64_t chunk = 16 / esz;
     auto operand_ok = [&](const void* X, bool trans, int64_t rows, int64_t ld, int64_t ld_b) {
         if (!aligned(X, 16) || ld % chunk != 0) return false;
-        if (trans) return rows % chunk == 0 && (K + 128) * ld_b + 512 < kMaxRowBytes;
+        // K-rows read reach K + 127 (BF16, 64 per stage) or K + 255 (FP8, 128)
+        if (trans) return rows % chunk == 0 && (K + 256 / esz) * ld_b + 512 < kMaxRowBytes;
         return K % chunk == 0 && ld_b * hk::kPP8Tile < kMaxRowBytes;
     };
     const bool fast_ok = operand_ok(A, at, M, lda, lda_b) && operand_ok(B, bt, N, ldb, ldb_b);
     const bool trans = at || bt;
     if (trans) {
-        // the 4-wave BF16 kernel reads K-strided images; BASIC reads anything
+        // the 4-wave BF16 and per-tensor FP8 kernels read K-strided images;
+        // BASIC reads anything
+        const bool il4_ok = dtype == HK_DTYPE_BF16 || dtype == HK_DTYPE_FP8_E4M3;
         if (sched == HK_SCHEDULE_AUTO)
-            sched = fast_ok && dtype == HK_DTYPE_BF16 ? HK_SCHEDULE_INTERLEAVE4 : HK_SCHEDULE_BASIC;
-        if (sched != HK_SCHEDULE_BASIC &&
-            (sched != HK_SCHEDULE_INTERLEAVE4 || dtype != HK_DTYPE_BF16))
+            sched = fast_ok && il4_ok ? HK_SCHEDULE_INTERLEAVE4 : HK_SCHEDULE_BASIC;
+        if (sched != HK_SCHEDULE_BASIC && (sched != HK_SCHEDULE_INTERLEAVE4 || !il4_ok))
             return HK_ERROR_NOT_SUPPORTED;
     }
     if (dtype == HK_DTYPE_MXFP8_E4M3) {
@@ -296,6 +317,15 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
         if (mx) {
             p->kernel = (const void*)hk_gemm_il4_mxfp8;
             p->name = "hk_gemm_il4_mxfp8";
+        } else if (fp8 && at && bt) {
+            p->kernel = (const void*)hk_gemm_il4_fp8_akm_bkn;
+            p->name = "hk_gemm_il4_fp8_akm_bkn";
+        } else if (fp8 && at) {
+            p->kernel = (const void*)hk_gemm_il4_fp8_akm;
+            p->name = "hk_gemm_il4_fp8_akm";
+        } else if (fp8 && bt) {
+            p->kernel = (const void*)hk_gemm_il4_fp8_bkn;
+            p->name = "hk_gemm_il4_fp8_bkn";
         } else if (fp8) {
             p->kernel = (const void*)hk_gemm_il4_fp8;
             p->name = "hk_gemm_il4_fp8";

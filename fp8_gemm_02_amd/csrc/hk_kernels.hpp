@@ -653,9 +653,29 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
 constexpr int kMxGroupStages = 4;
 constexpr uint32_t kMxGroupBytes = 2u * kIL4Tile * 16u;  // A and B scales of a group
 
-template <bool kMx>
+// kAT, kBT (per-tensor FP8 only): the operand is stored K-strided (A as K x M,
+// B as K x N, one byte per element, row stride lda or ldb).  A stage of such
+// an operand is 128 K-rows x 256 bytes (the tile's 256 rows of M or N); one
+// direct load covers four K-rows, and 16-byte chunk c of K-row k sits at
+// c ^ km8_key(k).  A fragment (16 rows, the lane's 32 K values) is built by
+// four transposing reads (ds_read_b64_tr_b8).  Within each group of 16 lanes,
+// output lane i's byte r comes from source lane 2r + i/8, byte i%8 of its 8
+// (measured on gfx950).  So source lane s of lane group g addresses K-row
+// 16g + s/2 (+ 8, + 64, + 72 for the other reads), the half s%2 of the
+// block's 16-byte chunk, and output lane i receives row i's 8 consecutive K
+// values: the same operand a K-contiguous image gives.  The key puts the 8
+// K-rows of one lane group on distinct chunks, and those of lane groups g
+// and g+1 on disjoint sets of chunks.
+__device__ __forceinline__ uint32_t km8_key(uint32_t k) {
+    return (k & 7u) | (((k >> 4) & 1u) << 3);
+}
+constexpr uint32_t kKM8RowBytes = kIL4Tile;    // one K-row of an 8-bit transposed stage image
+constexpr uint32_t kKM8StageRows = kRowBytes;  // 128 K-rows of E4M3 per stage
+
+template <bool kMx, bool kAT = false, bool kBT = false>
 __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf0,
                                              const IL4Buf buf1, HK_LDS uint8_t* scl) {
+    static_assert(!(kMx && (kAT || kBT)), "block scales take K-contiguous operands only");
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
@@ -670,17 +690,31 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     // 8b + l/8, physical chunk l%8 holding logical chunk (l%8) ^ (l/8); wave
     // w sends blocks w + 4j (j = 0..7) of A and of B.
     const uint32_t kc_lane = (lane & 7u) ^ (lane >> 3);
+    // K-strided operand: block b = K-rows 4b .. 4b+3 of the stage; lane l ->
+    // K-row 4b + l/16, physical chunk l%16
     uint32_t voff_a[8], voff_b[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t row = (wave + 4u * j) * 8u + (lane >> 3);
-        voff_a[j] = row * g.lda_b + kc_lane * 16u;
-        voff_b[j] = row * g.ldb_b + kc_lane * 16u;
+        const uint32_t krow = 4u * (wave + 4u * j) + (lane >> 4);
+        const uint32_t kmo = ((lane & 15u) ^ km8_key(krow)) * 16u;
+        voff_a[j] = kAT ? krow * g.lda_b + kmo : row * g.lda_b + kc_lane * 16u;
+        voff_b[j] = kBT ? krow * g.ldb_b + kmo : row * g.ldb_b + kc_lane * 16u;
     }
     struct Tile {
         i32x4 ra, rb;
         i32x4 rsa, rsb;  // MXFP8: the tile's scale rows
         int32_t m0, n0;
+    };
+    // rows r0 .. of an operand with `rows` rows: K-contiguous, the panel ends
+    // with row rows - 1; K-strided, it ends at K-row K - 1, row rows - 1
+    auto panel = [&](bool trans, const uint8_t* X, uint32_t ld_b, int32_t rows, int32_t r0,
+                     bool live) {
+        const uint64_t sz = !live   ? 0
+                            : trans ? (uint64_t)(g.K - 1) * ld_b + (uint64_t)(rows - r0)
+                                    : (uint64_t)(rows - r0) * ld_b;
+        const uint8_t* base = X + (trans ? (int64_t)r0 : (int64_t)r0 * ld_b);
+        return make_rsrc_words(base, (uint32_t)(sz > kOobOffset ? kOobOffset : sz));
     };
     auto tile = [&](uint32_t w) {
         Tile t;
@@ -688,12 +722,8 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         if (w < total) tile_of(w, g.grid, &tm, &tn);
         t.m0 = (int32_t)tm * kIL4Tile;
         t.n0 = (int32_t)tn * kIL4Tile;
-        const uint64_t sa = w < total ? (uint64_t)(g.M - t.m0) * g.lda_b : 0;
-        const uint64_t sb = w < total ? (uint64_t)(g.N - t.n0) * g.ldb_b : 0;
-        t.ra = make_rsrc_words(g.A + (int64_t)t.m0 * g.lda_b,
-                               (uint32_t)(sa > kOobOffset ? kOobOffset : sa));
-        t.rb = make_rsrc_words(g.B + (int64_t)t.n0 * g.ldb_b,
-                               (uint32_t)(sb > kOobOffset ? kOobOffset : sb));
+        t.ra = panel(kAT, g.A, g.lda_b, g.M, t.m0, w < total);
+        t.rb = panel(kBT, g.B, g.ldb_b, g.N, t.n0, w < total);
         if constexpr (kMx) {
             const uint64_t xa = w < total ? (uint64_t)(g.M - t.m0) * g.ldsa : 0;
             const uint64_t xb = w < total ? (uint64_t)(g.N - t.n0) * g.ldsb : 0;
@@ -739,11 +769,20 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
         uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
-        if constexpr (decltype(masked)::value) vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
+        uint32_t so = koff;
+        if (i < 8 ? kAT : kBT) {
+            // K-rows past K fall outside the buffer and read zeros; the
+            // stage's K-row offset goes into the VGPR offset, which the
+            // buffer range check covers
+            vo += s * kKM8StageRows * (i < 8 ? g.lda_b : g.ldb_b);
+            so = 0;
+        } else if constexpr (decltype(masked)::value) {
+            vo = koff + kc_lane * 16u < kbytes ? vo : kOobOffset;
+        }
         if (i < 8)
-            load_lds_b128(tt.ra, (HK_LDS void*)(d.a + blk * 64u), vo, koff);
+            load_lds_b128(tt.ra, (HK_LDS void*)(d.a + blk * 64u), vo, so);
         else
-            load_lds_b128(tt.rb, (HK_LDS void*)(d.b + blk * 64u), vo, koff);
+            load_lds_b128(tt.rb, (HK_LDS void*)(d.b + blk * 64u), vo, so);
     };
 
     // ---- LDS -> fragments: lane l holds row (block base + l%16), logical
@@ -754,11 +793,29 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     const uint32_t fo1 = r16 * kChunks + ((4u + g4) ^ (r16 & 7u));
     const uint32_t arow = wm * 128u;
     const uint32_t brow = wn * 128u;
+    // K-strided image: lane l (group g4, s = l%16) reads K-row 16 g4 + s/2
+    // (+ 8, + 64, + 72), half s%2 of the block's chunk; km8_key of those
+    // K-rows is (s/2) | (g4 % 2) << 3 for all four reads.
+    const uint32_t km8_kk = (r16 >> 1) | ((g4 & 1u) << 3);
+    const uint32_t km8_row = (16u * g4 + (r16 >> 1)) * kKM8RowBytes + (r16 & 1u) * 8u;
+    auto read_km8 = [&](const HK_LDS i32x4* img, uint32_t blk16) -> i32x8 {
+        const HK_LDS uint8_t* p = (const HK_LDS uint8_t*)img + km8_row + 16u * (blk16 ^ km8_kk);
+        i32x2 v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            v[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (HK_LDS i32x2*)(p + (uint32_t)(8 * (c & 1) + 64 * (c >> 1)) * kKM8RowBytes));
+        const i32x4 lo = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3);
+        const i32x4 hi = __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
     auto rd_a = [&](const IL4Buf& d, int mb) -> i32x8 {
+        if constexpr (kAT) return read_km8(d.a, arow / 16u + (uint32_t)mb);
         const HK_LDS i32x4* p = d.a + (arow + 16u * (uint32_t)mb) * kChunks;
         return __builtin_shufflevector(p[fo0], p[fo1], 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto rd_b = [&](const IL4Buf& d, int nb) -> i32x8 {
+        if constexpr (kBT) return read_km8(d.b, brow / 16u + (uint32_t)nb);
         const HK_LDS i32x4* p = d.b + (brow + 16u * (uint32_t)nb) * kChunks;
         return __builtin_shufflevector(p[fo0], p[fo1], 0, 1, 2, 3, 4, 5, 6, 7);
     };

@@ -29,6 +29,8 @@ Workloads (M x N x K, operands K-contiguous, A is M x K, B is N x K):
 * ``bf16_8192_akm_bkn`` the same with A stored K x M as well (C = A^T B with
                       the stored arrays);
 * ``bf16_8192_akm``   the bf16_8192 matrices with A stored K x M only.
+* ``fp8_8192_bkn``, ``fp8_8192_akm_bkn`` the fp8_8192 matrices with B (and A)
+  stored K-strided.
 
 Stored operands: a workload's layout_a / layout_b say how A and B sit in
 memory (0: rows of K, A as M x K and B as N x K; 1: A as K x M, B as K x N).
@@ -105,6 +107,8 @@ WORKLOADS = {
         Workload("bf16_8192_bkn", 2, 8192, 8192, 8192, "bf16", "normal002", 0, 1),
         Workload("bf16_8192_akm_bkn", 2, 8192, 8192, 8192, "bf16", "normal002", 1, 1),
         Workload("bf16_8192_akm", 2, 8192, 8192, 8192, "bf16", "normal002", 1, 0),
+        Workload("fp8_8192_bkn", 4, 8192, 8192, 8192, "fp8", "fp8_normal", 0, 1),
+        Workload("fp8_8192_akm_bkn", 4, 8192, 8192, 8192, "fp8", "fp8_normal", 1, 1),
     ]
 }
 

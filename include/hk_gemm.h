@@ -127,10 +127,12 @@ typedef enum hk_grid_order {
  *                 B(j, k) = B[k*ldb + j] (B stored K x N, ldb >= N).
  * C = sum_k A(i, k) B(j, k) in every case: A K_STRIDED gives A^T-style
  * products, B K_STRIDED gives C = A * B with B as stored, and both give the
- * pages' A^T * B.  K_STRIDED runs on INTERLEAVE4 (BF16; chosen by AUTO) or
- * BASIC.  INTERLEAVE4 needs, per K_STRIDED operand, 16-byte alignment, the
- * stride and M (or N) multiples of 8, and (K + 128) rows of stride below
- * 2^31 bytes; the other schedules return HK_ERROR_NOT_SUPPORTED for it.
+ * pages' A^T * B.  K_STRIDED runs on INTERLEAVE4 (BF16 and FP8 with
+ * per-tensor scales; chosen by AUTO) or BASIC.  INTERLEAVE4 needs, per
+ * K_STRIDED operand, 16-byte alignment, the stride and M (or N) in whole
+ * 16-byte chunks (multiples of 8 for BF16, of 16 for FP8), and (K + 128)
+ * rows (BF16) or (K + 256) rows (FP8) of stride below 2^31 bytes; the other
+ * schedules, and MXFP8, return HK_ERROR_NOT_SUPPORTED for it.
  */
 typedef enum hk_layout {
     HK_LAYOUT_K_CONTIGUOUS = 0,

@@ -161,11 +161,6 @@ def test_plan_strided_layout_other_schedules_unsupported():
     for sched in ("pingpong8", "smalltile", "interleave8", "producer_consumer"):
         with pytest.raises(hk.HKError):
             _plan(hk.HK_DTYPE_BF16, 1024, 1024, 1024, schedule=sched, layout_a=1, lda=1024)
-    # FP8 with a K-strided operand: the plain kernel only
-    p = _plan(hk.HK_DTYPE_FP8_E4M3, 1024, 1024, 1024, layout_b=1, ldb=1024)
-    assert p["kernel_name"] == "hk_gemm_basic_fp8"
-    with pytest.raises(hk.HKError):
-        _plan(hk.HK_DTYPE_FP8_E4M3, 1024, 1024, 1024, layout_b=1, ldb=1024, schedule="interleave4")
     p = _plan(hk.HK_DTYPE_BF16, 1024, 1024, 1024, layout_b=1, ldb=1024, schedule="basic")
     assert p["kernel_name"] == "hk_gemm_basic_bf16"
 
@@ -404,3 +399,28 @@ def test_attn_empty_is_a_noop_success(L):
     assert _attn(L, B=0, Q=0, K=0, V=0, O=0) == hk.HK_SUCCESS
     assert _attn(L, N=0, Q=0, K=0, V=0, O=0) == hk.HK_SUCCESS
     assert _attn(L, Hq=0, Q=0, K=0, V=0, O=0) == hk.HK_SUCCESS
+
+
+def test_plan_fp8_strided_layouts():
+    """FP8 (per-tensor scales) with K-strided operands runs on the 4-wave
+    kernel; other fast schedules and block scales refuse such operands."""
+    FP8 = hk.HK_DTYPE_FP8_E4M3
+    for la, lb, name in ((0, 1, "hk_gemm_il4_fp8_bkn"), (1, 0, "hk_gemm_il4_fp8_akm"),
+                         (1, 1, "hk_gemm_il4_fp8_akm_bkn")):
+        kw = dict(layout_a=la, layout_b=lb, lda=1024 if la else 1024, ldb=1024)
+        assert _plan(FP8, 1024, 1024, 1024, **kw)["kernel_name"] == name
+        assert _plan(FP8, 1024, 1024, 1024, schedule="interleave4", **kw)["kernel_name"] == name
+        for sched in ("pingpong8", "smalltile"):
+            with pytest.raises(hk.HKError):
+                _plan(FP8, 1024, 1024, 1024, schedule=sched, **kw)
+    # a K-strided N that is not whole 16-byte chunks: the plain kernel
+    assert _plan(FP8, 1024, 1000, 1024, layout_b=1, ldb=1000)["kernel_name"] == "hk_gemm_basic_fp8"
+    # K-rows up to K + 255 are read (128 per stage): the 31-bit offset bound
+    # is (K + 256) rows of B, tighter than BF16's K + 128
+    K = (1 << 21) - 192
+    assert (K + 128) * 1024 + 512 < 2 ** 31 <= (K + 256) * 1024 + 512
+    assert _plan(FP8, 1024, 1024, K, layout_b=1, ldb=1024)["kernel_name"] == "hk_gemm_basic_fp8"
+    assert _plan(FP8, 1024, 1024, K - 128, layout_b=1,
+                 ldb=1024)["kernel_name"] == "hk_gemm_il4_fp8_bkn"
+    with pytest.raises(hk.HKError):
+        _plan(hk.HK_DTYPE_MXFP8_E4M3, 1024, 1024, 1024, layout_b=1, ldb=1024)

@@ -10,8 +10,9 @@ ulp_bf16(C_ref) + 1e-4 * S.
 
 Shapes cover one tile, several tiles with ragged M and N, a K tail that is
 not a multiple of a stage (and, with both operands K-strided, not a multiple
-of 8), more tiles than compute units (the persistent walk), the plain
-fallback (a K-strided N that is not a multiple of 8, and FP8), the
+of 8), more tiles than compute units (the persistent walk), the same for FP8
+on its 4-wave kernel, the plain fallback (a K-strided M or N that is not
+whole 16-byte chunks, for BF16 and FP8), the
 A @ B convenience over torch views, and the 8192^3 workload with B stored
 K x N in the benchmark's launch configuration (sampled entries).
 """
@@ -154,9 +155,65 @@ def test_bf16_layouts_basic_fallback(layouts):
            expect_kernel="hk_gemm_basic_bf16")
 
 
+FAST8 = {(0, 1): "hk_gemm_il4_fp8_bkn", (1, 0): "hk_gemm_il4_fp8_akm",
+         (1, 1): "hk_gemm_il4_fp8_akm_bkn"}
+
+
+def _fp8(rows, cols, seed, integer):
+    X, s = gemm_inputs.fp8_matrix(rows, cols, seed, integer)
+    return X, (None if integer else s)
+
+
+def _check8(M, N, K, layouts, integer, seed, **kw):
+    A, sa = _fp8(M, K, seed, integer)
+    B, sb = _fp8(N, K, seed + 1, integer)
+    if integer:
+        sa, sb = 0.5, 2.0
+    return _check("fp8", A, B, M, N, K, *layouts, exact=integer, sa=sa, sb=sb, **kw)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (528, 608, 656), (16, 16, 16),
+                                   (272, 1008, 1296), (1040, 784, 144), (16, 528, 4160)])
+@pytest.mark.parametrize("layouts", LAYOUTS)
+@pytest.mark.parametrize("integer", [True, False])
+def test_fp8_layouts_full(M, N, K, layouts, integer):
+    """FP8 with K-strided operands on the 4-wave kernel (transposing 8-bit
+    LDS reads): ragged tiles and K tails."""
+    _check8(M, N, K, layouts, integer, 3 * M + K, expect_kernel=FAST8[layouts])
+
+
+@pytest.mark.parametrize("K", [100, 1, 37, 200, 300])
+def test_fp8_both_strided_any_k(K):
+    """Both operands K-strided: K-rows past K read zero through the buffer
+    bounds, so K needs no alignment."""
+    _check8(272, 528, K, (1, 1), True, 7 + K, expect_kernel=FAST8[(1, 1)])
+
+
+@pytest.mark.parametrize("layouts", LAYOUTS)
+def test_fp8_layouts_padded_strides_poisoned(layouts):
+    M, N, K = 528, 272, 400
+    la, lb = layouts
+    lda = (M if la else K) + 32
+    ldb = (N if lb else K) + 48
+    _check8(M, N, K, layouts, False, 61, lda=lda, ldb=ldb, expect_kernel=FAST8[layouts])
+
+
+@pytest.mark.parametrize("layouts", [(0, 1), (1, 0), (1, 1)])
+def test_fp8_layouts_persistent_walk(layouts):
+    _check8(4352, 4368, 640, layouts, True, 83, expect_kernel=FAST8[layouts])  # 17 x 18 tiles
+
+
+@pytest.mark.parametrize("layouts", LAYOUTS)
+@pytest.mark.parametrize("grid_order", ["row_major", "xcd"])
+def test_fp8_layouts_grid_orders(layouts, grid_order):
+    _check8(1040, 1296, 256, layouts, True, 93, grid_order=grid_order,
+            expect_kernel=FAST8[layouts])
+
+
 @pytest.mark.parametrize("layouts", LAYOUTS)
 @pytest.mark.parametrize("integer", [True, False])
 def test_fp8_layouts_basic(layouts, integer):
+    """A K-strided M or N that is not a multiple of 16 runs on the plain kernel."""
     M, N, K = 264, 392, 320
     A, sa = gemm_inputs.fp8_matrix(M, K, 41, integer)
     B, sb = gemm_inputs.fp8_matrix(N, K, 42, integer)
@@ -212,4 +269,33 @@ def test_bf16_8192_b_stored_kn_sampled():
                                  gemm_inputs.bits(x["B"]).ravel(), w.M, w.N, w.K, rows, cols)
     st = oracle.compare(got[rows, cols], ref, S, rel_tol=RTOL)
     _say("bf16_8192_bkn sampled", rows.size, {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
+
+
+def test_fp8_8192_b_stored_kn_sampled():
+    """The FP8 B-stored-K-x-N workload as the benchmark launches it (4-wave
+    kernel, transposing 8-bit reads), on sampled entries."""
+    w = gemm_inputs.WORKLOADS["fp8_8192_bkn"]
+    x = gemm_inputs.make_inputs(w)
+    A_st, B_st = gemm_inputs.stored(w, x)
+    A = A_st.cuda()
+    B = B_st.cuda()
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    plan = hk.hk_gemm_plan(hk.HK_DTYPE_FP8_E4M3, A, B, C, w.M, w.N, w.K, w.lda, w.ldb, w.N,
+                           layout_a=w.layout_a, layout_b=w.layout_b)
+    assert plan["kernel_name"] == "hk_gemm_il4_fp8_bkn"
+    hk.hk_gemm_ex(hk.HK_DTYPE_FP8_E4M3, A, B, C, w.M, w.N, w.K, w.lda, w.ldb, w.N,
+                  x["scale_a"], x["scale_b"], layout_a=w.layout_a, layout_b=w.layout_b)
+    torch.cuda.synchronize()
+    got = _bits16(C)
+    del A, B, C
+    rng = np.random.default_rng(5)
+    edge = np.array([0, 1, 255, 256, 4095, 4096, w.M - 256, w.M - 1])
+    rows = np.concatenate([rng.integers(0, w.M, 1500), np.repeat(edge, edge.size)])
+    cols = np.concatenate([rng.integers(0, w.N, 1500), np.tile(edge, edge.size)])
+    ref, S = oracle.gemm_sampled("fp8", gemm_inputs.bits(x["A"]).ravel(),
+                                 gemm_inputs.bits(x["B"]).ravel(), w.M, w.N, w.K, rows, cols,
+                                 scale_a=x["scale_a"], scale_b=x["scale_b"])
+    st = oracle.compare(got[rows, cols], ref, S, rel_tol=RTOL)
+    _say("fp8_8192_bkn sampled", rows.size, {k: st[k] for k in st if k != "ulp_hist"})
     assert st["ok"], st
