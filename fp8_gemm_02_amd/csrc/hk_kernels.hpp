@@ -942,11 +942,12 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         acc_settle();  // the last MFMA results before the epilogue reads them
 
         // ---- epilogue: lane holds C[m][n..n+3] of block (mb, nb), times sA*sB
-        const int32_t mrow = cur.m0 + (int32_t)(arow + r16);
+        const uint32_t le = lane_id_here();
+        const int32_t mrow = cur.m0 + (int32_t)(arow + (le & 15u));
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const int32_t m = mrow + mb * 16;
-            store_c_rows(g.C + (int64_t)m * g.ldc, m < g.M, cur.n0 + (int32_t)brow, g4, g.N,
+            store_c_rows(g.C + (int64_t)m * g.ldc, m < g.M, cur.n0 + (int32_t)brow, le >> 4, g.N,
                          acc[mb], g.scale, g.c_align);
         }
         if (w_next >= total) break;
