@@ -244,6 +244,30 @@ def test_matmul_infers_layouts_from_strides():
         assert st["ok"], (name, st)
 
 
+def test_matmul_fp8_views():
+    """hk.matmul on E4M3 tensors over all four storages (the 4-wave FP8
+    kernels, K-strided or not), bit-exact on integer-valued inputs."""
+    M, N, K = 272, 528, 208
+    A, _ = gemm_inputs.fp8_matrix(M, K, 53, True)    # logical A (M x K)
+    Bt, _ = gemm_inputs.fp8_matrix(N, K, 54, True)   # logical B^T (N x K)
+    sa, sb = 0.5, 2.0
+    ref, _ = oracle.gemm("fp8", gemm_inputs.bits(A).ravel(), gemm_inputs.bits(Bt).ravel(), M, N, K,
+                         scale_a=sa, scale_b=sb)
+    e4 = torch.float8_e4m3fn
+    A_mk = A.view(e4).cuda()
+    A_km = A.t().contiguous().view(e4).cuda()
+    B_nk = Bt.view(e4).cuda()
+    B_kn = Bt.t().contiguous().view(e4).cuda()
+    for a_view, b_view, name in [(A_mk, B_kn, "A @ B"), (A_mk, B_nk.t(), "A @ (N x K)^T"),
+                                 (A_km.t(), B_kn, "(K x M)^T @ B"),
+                                 (A_km.t(), B_nk.t(), "(K x M)^T @ (N x K)^T")]:
+        C = hk.matmul(a_view, b_view, scale_a=sa, scale_b=sb)
+        torch.cuda.synchronize()
+        st = oracle.compare(_bits16(C), ref, exact=True)
+        _say("matmul fp8", name, {k: st[k] for k in st if k != "ulp_hist"})
+        assert st["ok"], (name, st)
+
+
 def test_bf16_8192_b_stored_kn_sampled():
     """The B-stored-K-x-N workload exactly as the benchmark launches it,
     checked on sampled entries (random plus the corners of edge tiles)."""
