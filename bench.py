@@ -1,7 +1,8 @@
 """Benchmark: BF16 GEMM C = A * B^T at 8192^3 on one MI355X (TFLOP/s, % of 2.5 PF).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--schedule S] [--grid-order G] [--no-cpu-baseline] [--no-flush]
+                    [--schedule S] [--grid-order G] [--group-m G] [--window W]
+                    [--no-cpu-baseline] [--no-flush] [--library-context]
 
 A step is one call of the whole path (hk_gemm_bf16 / hk_gemm_fp8 through the
 C ABI) on inputs already resident in HBM.  W untimed steps, then exactly K
