@@ -61,6 +61,24 @@ __device__ __forceinline__ void load_lds_b128(i32x4 rsrc, HK_LDS void* lds_wave_
         : "memory", "m0");
 }
 
+// The same direct load through the global path: lane i fetches 16 bytes at
+// base + voffset, with no range check.  The address path of these is cheaper
+// than the buffer form's (measured: the sequencer's address FIFO toward the
+// texture unit was full 19 times less often in the BF16 GEMM), so the 4-wave
+// kernel uses them where every row and K chunk it loads lies inside the
+// operand; base is wave-uniform.
+__device__ __forceinline__ void load_lds_global_b128(const void* base, HK_LDS void* lds_wave_base,
+                                                     uint32_t voffset) {
+    const uint32_t m0v = (uint32_t)(uintptr_t)lds_wave_base;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(m0v), "v"(voffset), "s"(base)
+        : "memory", "m0");
+}
+
 // ------------------------------------------------------------ MFMA wrappers
 //
 // 16x16x32 bf16: each lane supplies 8 bf16 of one row of the 16 x 32 "A"

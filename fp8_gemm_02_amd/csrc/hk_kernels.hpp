@@ -442,11 +442,20 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     // (every lane, for a stage past the end) read zeros; the main loop, whose
     // stages all lie inside K, skips that select.
     const uint32_t krot = chiplet_k_rotation(nk_whole);
-    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i) {
+    // glob: the tile lies inside C and the stage inside K, so the unchecked
+    // global form of the load reads only the operands (K-contiguous only)
+    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i,
+                    auto glob) {
         const uint32_t s = rotated_stage(s0, krot, nk_whole);
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
         const bool km = i < 8 ? kAT : kBT;
+        if constexpr (decltype(glob)::value && !kAT && !kBT) {
+            const uint8_t* base = i < 8 ? g.A + (int64_t)tt.m0 * g.lda_b : g.B + (int64_t)tt.n0 * g.ldb_b;
+            load_lds_global_b128(base + koff, (HK_LDS void*)((i < 8 ? d.a : d.b) + blk * 64u),
+                                 i < 8 ? voff_a[i & 7] : voff_b[i & 7]);
+            return;
+        }
         const uint32_t ld_b = i < 8 ? g.lda_b : g.ldb_b;
         uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
         uint32_t so = koff;
@@ -535,33 +544,35 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     // slice 1 of a stage: MFMAs on fy, the 16 loads of stage s of tile tt
     // into cur, and the reads of the next stage's slice 0 from nxt into fx
     auto slice1 = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
-                      const IL4Buf& nxt) {
+                      const IL4Buf& nxt, auto glob) {
 #pragma unroll
         for (int q = 0; q < 64; ++q) {
             mfma(fy, q);
-            if ((q & 3) == 1) send(masked, tt, cur, s, q >> 2);
+            if ((q & 3) == 1) send(masked, tt, cur, s, q >> 2, glob);
             if ((q & 3) == 3) rd(fx, nxt, 0, q >> 2);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     // stage t (in cur; the next stage in nxt) loading stage s of tile tt
     auto stage = [&](auto masked, const Tile& tt, uint32_t s, const IL4Buf& cur,
-                     const IL4Buf& nxt) {
+                     const IL4Buf& nxt, auto glob) {
         slice0(cur);
         wait_lgkmcnt0();  // F(t, 1) is in registers: this wave is done with stage t
         wait_vmcnt0();    // this wave's share of stage t+1 has landed
         fenced_barrier();
-        slice1(masked, tt, s, cur, nxt);
+        slice1(masked, tt, s, cur, nxt, glob);
     };
 
     const std::true_type masked;
     const std::false_type unmasked;
     uint32_t w = blockIdx.x;
     Tile cur = tile(w);
+    const std::false_type checked;
+    const std::true_type unchecked;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, cur, buf0, 0, i);
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf0, 0, i, checked);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, cur, buf1, 1, i);
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf1, 1, i, checked);
     wait_vmcnt<16>();
     fenced_barrier();
 #pragma unroll
@@ -574,9 +585,18 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         // Stage pair (t, t+1) loads stages t+2 and t+3, all inside K while
         // t + 4 <= the number of whole stages.
         uint32_t t = 0;
-        for (; t + 4 <= nk_whole; t += 2) {
-            stage(unmasked, cur, t + 2, buf0, buf1);
-            stage(unmasked, cur, t + 3, buf1, buf0);
+        // a tile inside C: its whole stages take the global loads
+        const bool inside = cur.m0 + kIL4Tile <= g.M && cur.n0 + kIL4Tile <= g.N;
+        if (!kAT && !kBT && inside) {
+            for (; t + 4 <= nk_whole; t += 2) {
+                stage(unmasked, cur, t + 2, buf0, buf1, unchecked);
+                stage(unmasked, cur, t + 3, buf1, buf0, unchecked);
+            }
+        } else {
+            for (; t + 4 <= nk_whole; t += 2) {
+                stage(unmasked, cur, t + 2, buf0, buf1, checked);
+                stage(unmasked, cur, t + 3, buf1, buf0, checked);
+            }
         }
         // the last pairs: stages at or past the end of this tile's K load
         // the next tile's first two stages (stage s of this tile is stage
@@ -592,9 +612,9 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         for (; t < nk_pad; t += 2) {
             uint32_t s0, s1;
             const Tile t0 = pick(t + 2, &s0);
-            stage(masked, t0, s0, buf0, buf1);
+            stage(masked, t0, s0, buf0, buf1, checked);
             const Tile t1 = pick(t + 3, &s1);
-            stage(masked, t1, s1, buf1, buf0);
+            stage(masked, t1, s1, buf1, buf0, checked);
         }
         acc_settle();  // the last MFMA results before the epilogue reads them
 
@@ -764,10 +784,19 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         return v;
     };
     const uint32_t krot = kMx ? 0u : chiplet_k_rotation(nk_whole);
-    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i) {
+    // glob: the tile lies inside C and the stage inside K, so the unchecked
+    // global form of the load reads only the operands (K-contiguous FP8 only)
+    auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i,
+                    auto glob) {
         const uint32_t s = rotated_stage(s0, krot, nk_whole);
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
+        if constexpr (decltype(glob)::value && !kMx && !kAT && !kBT) {
+            const uint8_t* base = i < 8 ? g.A + (int64_t)tt.m0 * g.lda_b : g.B + (int64_t)tt.n0 * g.ldb_b;
+            load_lds_global_b128(base + koff, (HK_LDS void*)((i < 8 ? d.a : d.b) + blk * 64u),
+                                 i < 8 ? voff_a[i & 7] : voff_b[i & 7]);
+            return;
+        }
         uint32_t vo = i < 8 ? voff_a[i & 7] : voff_b[i & 7];
         uint32_t so = koff;
         if (i < 8 ? kAT : kBT) {
@@ -863,11 +892,11 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     // slice 1 of stage t (in cur; stage t+1 in nxt, stage u1 of the tile whose
     // groups start at sequence sq1), loading stage s of tile tt (groups from ss)
     auto slice1 = [&](auto masked, const Tile& tt, uint32_t s, uint32_t ss, const IL4Buf& cur,
-                      const IL4Buf& nxt, uint32_t u1, uint32_t sq1) {
+                      const IL4Buf& nxt, uint32_t u1, uint32_t sq1, auto glob) {
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
             mfma(4 + (q & 3), q >> 2);
-            if (q & 1) send(masked, tt, cur, s, q >> 1);
+            if (q & 1) send(masked, tt, cur, s, q >> 1, glob);
             else if ((q & 3) == 0 && q > 0) get_b(masked, nxt, (q >> 2) - 1, u1, sq1);
             else if (q == 2) get_a(masked, nxt, 0, u1, sq1);
             else if (q == 6) get_a(masked, nxt, 1, u1, sq1);
@@ -879,23 +908,25 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     // stage t of the current tile; stage t+1 is stage u1 of the tile with group
     // sequence sq1 (this tile, or the next one past the end of K)
     auto stage = [&](auto masked, uint32_t t, const Tile& tt, uint32_t s, uint32_t ss,
-                     const IL4Buf& cur, const IL4Buf& nxt, uint32_t u1, uint32_t sq1) {
+                     const IL4Buf& cur, const IL4Buf& nxt, uint32_t u1, uint32_t sq1, auto glob) {
         slice0(masked, cur, t);
         wait_lgkmcnt0();  // A(t, 2-7) are in registers: this wave is done with stage t
         wait_vmcnt0();    // this wave's share of stage t+1 has landed
         fenced_barrier();
-        slice1(masked, tt, s, ss, cur, nxt, u1, sq1);
+        slice1(masked, tt, s, ss, cur, nxt, u1, sq1, glob);
     };
 
     const std::true_type masked;
     const std::false_type unmasked;
     uint32_t w = blockIdx.x;
     Tile cur = tile(w);
+    const std::false_type checked;
+    const std::true_type unchecked;
     send_scales(cur, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, cur, buf0, 0, i);
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf0, 0, i, checked);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) send(masked, cur, buf1, 1, i);
+    for (int i = 0; i < 16; ++i) send(masked, cur, buf1, 1, i, checked);
     wait_vmcnt<16>();
     fenced_barrier();
     get_a(masked, buf0, 0, 0, 0);
@@ -908,9 +939,18 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         const uint32_t w_next = w + gridDim.x;
         const Tile nxt = tile(w_next);
         uint32_t t = 0;
-        for (; t + 4 <= nk_whole; t += 2) {
-            stage(unmasked, t, cur, t + 2, seq, buf0, buf1, t + 1, seq);
-            stage(unmasked, t + 1, cur, t + 3, seq, buf1, buf0, t + 2, seq);
+        // a tile inside C: its whole stages take the global loads
+        const bool inside = cur.m0 + kIL4Tile <= g.M && cur.n0 + kIL4Tile <= g.N;
+        if (!kMx && !kAT && !kBT && inside) {
+            for (; t + 4 <= nk_whole; t += 2) {
+                stage(unmasked, t, cur, t + 2, seq, buf0, buf1, t + 1, seq, unchecked);
+                stage(unmasked, t + 1, cur, t + 3, seq, buf1, buf0, t + 2, seq, unchecked);
+            }
+        } else {
+            for (; t + 4 <= nk_whole; t += 2) {
+                stage(unmasked, t, cur, t + 2, seq, buf0, buf1, t + 1, seq, checked);
+                stage(unmasked, t + 1, cur, t + 3, seq, buf1, buf0, t + 2, seq, checked);
+            }
         }
         // stages at or past the end of this tile's K load the next tile's
         // first two (stage s of this tile is stage s - nk_pad of the next)
@@ -931,13 +971,13 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
             uint32_t s0, s1;
             const Tile t0 = pick(t + 2, &s0);
             const uint32_t q0 = t + 2 < nk_pad ? seq : seq_next;
-            stage(masked, t, t0, s0, q0, buf0, buf1, t + 1, seq);
+            stage(masked, t, t0, s0, q0, buf0, buf1, t + 1, seq, checked);
             const Tile t1 = pick(t + 3, &s1);
             const uint32_t q1 = t + 3 < nk_pad ? seq : seq_next;
             // stage t+2 is the next tile's stage 0 once t+2 reaches the end
             const uint32_t u2 = t + 2 < nk_pad ? t + 2 : 0u;
             const uint32_t qu = t + 2 < nk_pad ? seq : seq_next;
-            stage(masked, t + 1, t1, s1, q1, buf1, buf0, u2, qu);
+            stage(masked, t + 1, t1, s1, q1, buf1, buf0, u2, qu, checked);
         }
         acc_settle();  // the last MFMA results before the epilogue reads them
 
