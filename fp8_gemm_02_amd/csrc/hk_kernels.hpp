@@ -443,16 +443,21 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
     // stages all lie inside K, skips that select.
     const uint32_t krot = chiplet_k_rotation(nk_whole);
     // glob: the tile lies inside C and the stage inside K, so the unchecked
-    // global form of the load reads only the operands (K-contiguous only)
+    // global form of the load reads only the operands
     auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i,
                     auto glob) {
         const uint32_t s = rotated_stage(s0, krot, nk_whole);
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
         const bool km = i < 8 ? kAT : kBT;
-        if constexpr (decltype(glob)::value && !kAT && !kBT) {
-            const uint8_t* base = i < 8 ? g.A + (int64_t)tt.m0 * g.lda_b : g.B + (int64_t)tt.n0 * g.ldb_b;
-            load_lds_global_b128(base + koff, (HK_LDS void*)((i < 8 ? d.a : d.b) + blk * 64u),
+        if constexpr (decltype(glob)::value) {
+            const uint8_t* x = i < 8 ? g.A : g.B;
+            const uint32_t ld_b = i < 8 ? g.lda_b : g.ldb_b;
+            const int64_t r0 = i < 8 ? tt.m0 : tt.n0;
+            // K-strided: the stage's first K-row, the tile's first column
+            const uint8_t* base = km ? x + r0 * 2 + (int64_t)s * kKMStageRows * ld_b
+                                     : x + r0 * ld_b + koff;
+            load_lds_global_b128(base, (HK_LDS void*)((i < 8 ? d.a : d.b) + blk * 64u),
                                  i < 8 ? voff_a[i & 7] : voff_b[i & 7]);
             return;
         }
@@ -587,7 +592,7 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         uint32_t t = 0;
         // a tile inside C: its whole stages take the global loads
         const bool inside = cur.m0 + kIL4Tile <= g.M && cur.n0 + kIL4Tile <= g.N;
-        if (!kAT && !kBT && inside) {
+        if (inside) {
             for (; t + 4 <= nk_whole; t += 2) {
                 stage(unmasked, cur, t + 2, buf0, buf1, unchecked);
                 stage(unmasked, cur, t + 3, buf1, buf0, unchecked);
@@ -785,15 +790,23 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     };
     const uint32_t krot = kMx ? 0u : chiplet_k_rotation(nk_whole);
     // glob: the tile lies inside C and the stage inside K, so the unchecked
-    // global form of the load reads only the operands (K-contiguous FP8 only)
+    // global form of the load reads only the operands.  MXFP8 and the kernels
+    // with A K-strided keep the buffer form: measured, it was as fast for
+    // MXFP8 and faster with A stored K x M.
     auto send = [&](auto masked, const Tile& tt, const IL4Buf& d, uint32_t s0, int i,
                     auto glob) {
         const uint32_t s = rotated_stage(s0, krot, nk_whole);
         const uint32_t koff = s * (uint32_t)kRowBytes;
         const uint32_t blk = wave + 4u * (uint32_t)(i & 7);
-        if constexpr (decltype(glob)::value && !kMx && !kAT && !kBT) {
-            const uint8_t* base = i < 8 ? g.A + (int64_t)tt.m0 * g.lda_b : g.B + (int64_t)tt.n0 * g.ldb_b;
-            load_lds_global_b128(base + koff, (HK_LDS void*)((i < 8 ? d.a : d.b) + blk * 64u),
+        if constexpr (decltype(glob)::value && !kMx && !kAT) {
+            const bool km = i < 8 ? kAT : kBT;
+            const uint8_t* x = i < 8 ? g.A : g.B;
+            const uint32_t ld_b = i < 8 ? g.lda_b : g.ldb_b;
+            const int64_t r0 = i < 8 ? tt.m0 : tt.n0;
+            // K-strided: the stage's first K-row, the tile's first column
+            const uint8_t* base = km ? x + r0 + (int64_t)s * kKM8StageRows * ld_b
+                                     : x + r0 * ld_b + koff;
+            load_lds_global_b128(base, (HK_LDS void*)((i < 8 ? d.a : d.b) + blk * 64u),
                                  i < 8 ? voff_a[i & 7] : voff_b[i & 7]);
             return;
         }
@@ -941,7 +954,7 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         uint32_t t = 0;
         // a tile inside C: its whole stages take the global loads
         const bool inside = cur.m0 + kIL4Tile <= g.M && cur.n0 + kIL4Tile <= g.N;
-        if (!kMx && !kAT && !kBT && inside) {
+        if (!kMx && !kAT && inside) {
             for (; t + 4 <= nk_whole; t += 2) {
                 stage(unmasked, t, cur, t + 2, seq, buf0, buf1, t + 1, seq, unchecked);
                 stage(unmasked, t + 1, cur, t + 3, seq, buf1, buf0, t + 2, seq, unchecked);
