@@ -286,6 +286,39 @@ def test_k_order_does_not_change_exact_results(dtype):
         assert st["ok"], (opts, st)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M", [768, 769])
+def test_interior_and_edge_tiles_with_padded_rows(dtype, M):
+    """The 4-wave kernels load the whole K stages of a tile that lies inside
+    C without a range check; edge tiles and the K tail keep the checked
+    loads.  With every tile inside C (M = 768, N = 512) and with a row of
+    edge tiles (M = 769), operands whose rows are padded past K with a poison
+    value must give the oracle's bits on integer-valued inputs: no load may
+    read the padding."""
+    N = 512
+    K, pad = (1000, 8) if dtype == "bf16" else (1936, 16)
+    if dtype == "bf16":
+        A, B, sa, sb = _bf16(M, K, "int4", 91), _bf16(N, K, "int4", 92), 1.0, 1.0
+        dt = hk.HK_DTYPE_BF16
+    else:
+        A, _ = gemm_inputs.fp8_matrix(M, K, 93, integer=True)
+        B, _ = gemm_inputs.fp8_matrix(N, K, 94, integer=True)
+        sa, sb, dt = 0.5, 4.0, hk.HK_DTYPE_FP8_E4M3
+    ref, _ = oracle.gemm(dtype, gemm_inputs.bits(A).ravel(), gemm_inputs.bits(B).ravel(), M, N, K,
+                         scale_a=sa, scale_b=sb)
+
+    def padded(X):
+        P = torch.full((X.shape[0], K + pad), 64.0).to(X.dtype)
+        P[:, :K] = X
+        return P.cuda()
+
+    _say("interior/edge tiles, padded rows", dtype, (M, N, K), "ld", K + pad)
+    C = _run(dt, padded(A), padded(B), M, N, K, K + pad, K + pad, N, sa, sb,
+             schedule="interleave4")
+    st = oracle.compare(_bits16(C), ref, exact=True)
+    assert st["ok"], st
+
+
 def test_zero_k_writes_zeros_and_empty_is_noop():
     C = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
     hk.hk_gemm_bf16(0, 0, C, 5, 7, 0, 1, 1, 7)
