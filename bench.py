@@ -2,16 +2,35 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--schedule S] [--grid-order G] [--group-m G] [--window W]
-                    [--no-cpu-baseline] [--no-flush] [--library-context]
+                    [--no-settle] [--no-cpu-baseline] [--no-flush] [--library-context]
 
 A step is one call of the whole path (hk_gemm_bf16 / hk_gemm_fp8 through the
-C ABI) on inputs already resident in HBM.  W untimed steps, then exactly K
-timed steps bracketed by device synchronisation; `value` is 2*M*N*K*steps /
-elapsed.  Each launch is also bracketed by HIP events on its own stream, and
-the mean event duration gives `roofline.achieved`.  After the timed region,
-launches preceded by a 1 GiB fill (which evicts L2 and the last-level cache)
-are timed the same way and reported as `flushed_kernel_ms`.  The CPU baseline
-times the FP64 oracle on a bounded sample of output rows on the host cores.
+C ABI) on inputs already resident in HBM.  Order of a run:
+
+  1. settle: the step runs in windows until the chip's clock has settled
+     (two consecutive windows within 1 % of each other after at least 60 ms
+     of GPU time, at most 1.5 s).  After idle, MI355X boosts its clock, then
+     its power controller pulls it well below the sustained level under this
+     power-bound load and brings it back over some tens of milliseconds: at
+     8192^3 single launches measured 0.75, 0.71, then up to 0.94 and back to
+     0.69 ms over about 40 launches, the chiplet clocks 1.72, then 1.24, then
+     1.70 GHz.  Any idle gap of a millisecond or so starts this again, and a
+     handful of warm-up steps ends inside the dip.  Each window is queued
+     before the previous one is read; the window means are under `settle`.
+  2. W untimed warm-up steps, queued right behind the last settle window.
+  3. exactly K timed steps back to back, bracketed by device synchronisation
+     and by one pair of HIP events on the launch stream, launched as soon as
+     the queue has drained, with every argument built beforehand; `value` is
+     2*M*N*K*K / wall time, `roofline.achieved` uses the event time / K.
+     The 4-wave kernels record their clocks in every timed launch
+     (hk_gemm_opts.clock_stamps, which costs nothing measurable): `clock_ghz`.
+  4. K more launches, each bracketed by its own events (per-launch events
+     cost about 5 us of gap per launch, so they stay out of the timed
+     region): `launch_ms` holds their deciles and the first ones in order.
+  5. launches each preceded by a 1 GiB fill (evicting L2 and the last-level
+     cache), `flushed_kernel_ms`.
+  6. the CPU baseline: the FP64 oracle on a bounded sample of output rows.
+
 `inputs` holds the SHA-256 of the operand bytes.  Prints one JSON line.
 """
 from __future__ import annotations
@@ -40,6 +59,8 @@ def parse():
     ap.add_argument("--grid-order", default="auto")
     ap.add_argument("--group-m", type=int, default=0)
     ap.add_argument("--window", type=int, default=0)
+    ap.add_argument("--no-settle", action="store_true",
+                    help="skip the clock-settling launches before the warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -129,7 +150,7 @@ def cpu_baseline(w, x, seconds: float):
     t = run(rows)
     flops = 2.0 * rows * w.N * w.K
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "cpu_model": cpu_model(), **host_cpus(threads),
             "sample": "%d of %d output rows (all %d columns, K=%d), FP64 scalar oracle, %.1f s"
                       % (rows, w.M, w.N, w.K, t)}
 
@@ -189,6 +210,142 @@ def library_context(a, w, A, B, sa, sb, stream, SA=None, SB=None):
     mean_ms = sum(durs) / len(durs)
     return {"library": name, "tflops": round(w.flops / (mean_ms * 1e-3) / 1e12, 2),
             "kernel_ms": {"mean": round(mean_ms, 4), "median": round(durs[len(durs) // 2], 4)}}
+
+
+def settle(step, stream, min_ms: float = 60.0, max_ms: float = 1500.0, tol: float = 0.01):
+    """Launch the step in windows until two consecutive window means agree.
+
+    Stops once at least min_ms of GPU time has passed and the last two windows'
+    mean launch times are within tol of each other, or after max_ms.  A window
+    is at least 10 launches and about 5 ms.  The next window is always queued
+    before the previous one is read, so the GPU never idles in between (an
+    idle gap of a millisecond or less starts the boost and clamp again).
+    Returns what it saw; the last queued window may still be running.
+    """
+    import torch
+
+    def window(n):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            s.record(stream)
+            for _ in range(n):
+                step()
+            e.record(stream)
+        return s, e, n
+
+    means, launches, gpu_ms = [], 0, 0.0
+    inflight = window(10)
+    while True:
+        s, e, n = inflight
+        inflight = window(int(min(1000, max(10, 5.0 / max(means[-1], 1e-4)))) if means else 10)
+        e.synchronize()
+        ms = s.elapsed_time(e)
+        means.append(ms / n)
+        launches += n
+        gpu_ms += ms
+        if gpu_ms >= max_ms:
+            break
+        if gpu_ms >= min_ms and len(means) >= 2 and abs(means[-1] - means[-2]) <= tol * means[-2]:
+            break
+    launches += inflight[2]
+    return {"launches": launches, "gpu_ms_measured": round(gpu_ms, 2),
+            "window_mean_ms": [round(m, 4) for m in means],
+            "rule": "windows of >= 10 launches (~5 ms), each queued before the previous is read, "
+                    "until two consecutive means agree within 1 %% after >= %.0f ms of GPU time, "
+                    "at most %.0f ms" % (min_ms, max_ms)}
+
+
+def series_events(n: int):
+    import torch
+    return ([torch.cuda.Event(enable_timing=True) for _ in range(n)],
+            [torch.cuda.Event(enable_timing=True) for _ in range(n)])
+
+
+def launch_series(step, stream, events):
+    """Launches each bracketed by its own pair of (pre-built) events: durations in ms, in order.
+
+    Queued at once after the previous synchronisation, so that the GPU idles
+    as little as possible in between.
+    """
+    import torch
+    starts, ends = events
+    n = len(starts)
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [s_.elapsed_time(e) for s_, e in zip(starts, ends)]
+
+
+def clock_summary(hk, stamps):
+    """Mean shader clock per chiplet over the timed launches, from their clock records."""
+    if stamps is None:
+        return None
+    khz = hk.hk_wall_clock_khz()
+    rows = stamps.cpu().tolist()
+    per = [hk.chiplet_clocks_ghz(r, khz) for r in rows]
+    chip = []
+    for x in range(8):
+        v = [p[x] for p in per if p[x] is not None]
+        chip.append(round(sum(v) / len(v), 3) if v else None)
+    launch = [sum(c for c in p if c is not None) / max(1, sum(c is not None for c in p))
+              for p in per]
+    return {"per_chiplet_mean": chip,
+            "launch_mean_first_last": [round(launch[0], 3), round(launch[-1], 3)],
+            "mean": round(sum(launch) / len(launch), 3), "wall_clock_khz": khz,
+            "how": "s_memtime / s_memrealtime spans of the first workgroup on each chiplet, "
+                   "recorded by the kernel in every timed launch"}
+
+
+def series_summary(durs):
+    """Mean, deciles and the first launches in order, in ms."""
+    srt = sorted(durs)
+    q = lambda f: srt[min(len(srt) - 1, int(round(f * (len(srt) - 1))))]
+    return {"launches": len(durs), "mean": round(sum(durs) / len(durs), 4),
+            "min": round(srt[0], 4),
+            "deciles": [round(q(i / 10.0), 4) for i in range(1, 10)],
+            "max": round(srt[-1], 4),
+            "first_in_order": [round(d, 4) for d in durs[:10]]}
+
+
+def timed_region(step, stream, steps: int, stamps=None, before=None):
+    """Exactly `steps` launches back to back: (wall seconds, event ms per launch).
+
+    With stamps (a steps x 32 device tensor), launch i records its clocks in
+    row i.  before() queues the untimed launches that precede the region; the
+    region starts right after they drain, with everything it needs built.
+    """
+    import torch
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rows = [None] * steps if stamps is None else [stamps[i] for i in range(steps)]
+    if before is not None:
+        before()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        s.record(stream)
+        if stamps is None:
+            for _ in range(steps):
+                step()
+        else:
+            for r in rows:
+                step(r)
+        e.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, s.elapsed_time(e) / steps
+
+
+def host_cpus(threads: int) -> dict:
+    """What the host offers next to the threads the oracle used."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = None
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": aff,
+            "threads_rule": "the affinity set, capped at 16 threads (one GPU's share of the "
+                            "host's cores); used %d" % threads}
 
 
 def cpu_model() -> str:
@@ -251,34 +408,33 @@ def main():
         def step():
             hk.hk_gemm_mxfp8(A, B, C, w.M, w.N, w.K, w.K, w.K, w.N, SA, SB, nb, nb, stream=stream)
     else:
-        def step():
+        def step(stamps=None):
             hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.lda, w.ldb, w.N, sa, sb,
-                          stream=stream, **opts)
+                          stream=stream, clock_stamps=stamps, **opts)
 
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(a.warmup):
-            step()
-    torch.cuda.synchronize()
-    print("[bench] warmup done (%d steps), timing %d" % (a.warmup, a.steps), file=sys.stderr,
+    # the 4-wave kernels write a clock record per launch (32 words each)
+    stamps = (torch.zeros((a.steps, 32), dtype=torch.int64, device=dev)
+              if w.dtype != "mxfp8" and plan["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4 else None)
+    print("[bench] settle, %d warm-up steps, %d timed" % (a.warmup, a.steps), file=sys.stderr,
           flush=True)
+    torch.cuda.synchronize()
+    settled = {}
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for i in range(a.steps):
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    durs_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    mean_ms = sum(durs_ms) / len(durs_ms)
+    def before():
+        # settle, then the warm-up steps queued behind its last window
+        if not a.no_settle:
+            settled.update(settle(step, stream))
+        with torch.cuda.stream(stream):
+            for _ in range(a.warmup):
+                step()
+
+    sev = series_events(a.steps)
+    elapsed, event_ms = timed_region(step, stream, a.steps, stamps, before)
+    series = launch_series(step, stream, sev)
+    settled = settled or None
     flops = w.flops
     value = flops * a.steps / elapsed / 1e12
-    achieved = flops / (mean_ms * 1e-3) / 1e12
+    achieved = flops / (event_ms * 1e-3) / 1e12
 
     out = {
         "metric": ("GEMM TFLOP/s at BF16 8192^3 and % of 2.5 PF BF16 peak (1 MI355X)"
@@ -302,8 +458,10 @@ def main():
                    "schedule": plan["schedule"], "grid_order": plan["grid_order"],
                    "group_m": plan["group_m"], "window": plan["window"]},
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS[w.dtype], 2),
-        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(durs_ms[len(durs_ms) // 2], 4),
-                      "min": round(durs_ms[0], 4), "max": round(durs_ms[-1], 4)},
+        "event_ms_per_step": round(event_ms, 4),
+        "launch_ms": series_summary(series),
+        "settle": settled,
+        "clock_ghz": clock_summary(hk, stamps),
         "inputs": inputs,
     }
     tr = traffic_from_profiles(plan["kernel_name"], w.name)
@@ -317,7 +475,7 @@ def main():
                            "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                            "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
     else:
-        gbs = w.algorithmic_bytes / (mean_ms * 1e-3) / 1e9
+        gbs = w.algorithmic_bytes / (event_ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     out["roofline"].update({"traffic": tr[1] if tr else None,
@@ -378,7 +536,7 @@ def cpu_baseline_attn(w, x, seconds: float):
     n = int(max(threads, min(nrow, seconds / max(t / (8 * threads), 1e-9))))
     t, flops = run(n)
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "cpu_model": cpu_model(), **host_cpus(threads),
             "sample": "%d random query rows of %d (all their visible keys), FP64 scalar oracle, "
                       "%.1f s" % (n, nrow, t)}
 
@@ -403,28 +561,24 @@ def bench_attn(a, w):
         hk.hk_attn_fwd_bf16(q, k, v, O, L, w.B, w.Hq, w.Hkv, w.N, w.D, w.scale, w.causal,
                             stream=stream)
 
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for _ in range(a.warmup):
-            step()
-    torch.cuda.synchronize()
-    print("[bench] warmup done (%d steps), timing %d" % (a.warmup, a.steps), file=sys.stderr,
+    print("[bench] settle, %d warm-up steps, %d timed" % (a.warmup, a.steps), file=sys.stderr,
           flush=True)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        for i in range(a.steps):
-            starts[i].record(stream)
-            step()
-            ends[i].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    durs_ms = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
-    mean_ms = sum(durs_ms) / len(durs_ms)
+    settled = {}
+
+    def before():
+        if not a.no_settle:
+            settled.update(settle(step, stream))
+        with torch.cuda.stream(stream):
+            for _ in range(a.warmup):
+                step()
+
+    sev = series_events(a.steps)
+    elapsed, event_ms = timed_region(step, stream, a.steps, None, before)
+    series = launch_series(step, stream, sev)
+    settled = settled or None
     value = w.flops * a.steps / elapsed / 1e12
-    achieved = w.flops / (mean_ms * 1e-3) / 1e12
+    achieved = w.flops / (event_ms * 1e-3) / 1e12
     tr = traffic_from_profiles(kernel, w.name)
     out = {
         "metric": "attention forward TFLOP/s, BF16 B=%d Hq=%d Hkv=%d N=%d D=%d %s (1 MI355X)"
@@ -445,8 +599,9 @@ def bench_attn(a, w):
                    "distribution": "normal", "kernel": kernel,
                    "flops_counted": "4 * D per visible (query, key) pair"},
         "pct_of_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 2),
-        "kernel_ms": {"mean": round(mean_ms, 4), "median": round(durs_ms[len(durs_ms) // 2], 4),
-                      "min": round(durs_ms[0], 4), "max": round(durs_ms[-1], 4)},
+        "event_ms_per_step": round(event_ms, 4),
+        "launch_ms": series_summary(series),
+        "settle": settled,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
                      "traffic": tr[1] if tr else None,

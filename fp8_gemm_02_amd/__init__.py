@@ -46,7 +46,8 @@ GRID_ORDERS = {"auto": 0, "row_major": 1, "xcd": 2}
 LAYOUTS = {"k_contiguous": 0, "k_strided": 1}
 
 EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-            "hk_grid_map", "hk_status_string", "hk_version", "hk_attn_fwd_bf16")
+            "hk_grid_map", "hk_status_string", "hk_version", "hk_wall_clock_khz",
+            "hk_attn_fwd_bf16")
 
 
 class HKError(RuntimeError):
@@ -59,7 +60,7 @@ class GemmOpts(ctypes.Structure):
     _fields_ = [("schedule", ctypes.c_int32), ("grid_order", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("clock_stamps", ctypes.c_void_p)]
 
 
 class AttnStrides(ctypes.Structure):
@@ -107,10 +108,11 @@ def lib():
     L.hk_status_string.argtypes = [i32]
     L.hk_status_string.restype = ctypes.c_char_p
     L.hk_version.argtypes = []
+    L.hk_wall_clock_khz.argtypes = []
     L.hk_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32,
                                    ctypes.POINTER(AttnStrides), vp]
     for name in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-                 "hk_grid_map", "hk_version", "hk_attn_fwd_bf16"):
+                 "hk_grid_map", "hk_version", "hk_wall_clock_khz", "hk_attn_fwd_bf16"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -137,7 +139,8 @@ def _stream(s) -> int:
     return int(s.cuda_stream)
 
 
-def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0):
+def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
+          clock_stamps=None):
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
     if isinstance(grid_order, str):
@@ -147,6 +150,7 @@ def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0)
     o = GemmOpts()
     o.schedule, o.grid_order, o.group_m, o.window = schedule, grid_order, group_m, window
     o.layout_a, o.layout_b = layout_a, layout_b
+    o.clock_stamps = _ptr(clock_stamps) or None
     return o
 
 
@@ -178,8 +182,10 @@ def hk_gemm_mxfp8(A, B, C, M, N, K, lda, ldb, ldc, scales_a, scales_b, ld_scales
 
 def hk_gemm_ex(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,
                schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
-               stream=None, raise_on_error=True):
-    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b)
+               stream=None, raise_on_error=True, clock_stamps=None):
+    """clock_stamps: None, or a 16-byte aligned device buffer of 32 uint64 (a
+    torch tensor or a pointer) for the launch's clock record."""
+    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b, clock_stamps)
     st = lib().hk_gemm_ex(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                           float(scale_a), float(scale_b), ctypes.byref(o), _stream(stream))
     return _check(st, "hk_gemm_ex", raise_on_error)
@@ -212,6 +218,26 @@ def hk_grid_map(grid_order, tiles_m, tiles_n, group_m, window, nxcd, wg):
 
 def hk_version() -> int:
     return int(lib().hk_version())
+
+
+def hk_wall_clock_khz() -> int:
+    """Rate of the constant-rate counter in the clock record, kHz (0 = unknown)."""
+    return int(lib().hk_wall_clock_khz())
+
+
+def chiplet_clocks_ghz(stamps, wall_khz: int):
+    """Mean shader clock of each chiplet over one launch, from its clock record.
+
+    stamps: 32 integers as written by the 4-wave kernels (see hk_gemm_opts);
+    chiplets whose workgroup did not record (zero spans) are None.
+    """
+    out = []
+    for x in range(8):
+        t0, r0, t1, r1 = (int(v) for v in stamps[4 * x:4 * x + 4])
+        dr = r1 - r0
+        out.append(None if dr <= 0 or t1 <= t0 or wall_khz <= 0
+                   else (t1 - t0) / dr * wall_khz * 1e3 / 1e9)
+    return out
 
 
 def gemm_nt(A, B, scale_a=None, scale_b=None, out=None, stream=None, **opts):

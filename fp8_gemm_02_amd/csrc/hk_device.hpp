@@ -48,17 +48,20 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t byte
 // inline assembly so that the compiler does not track the LDS write: the
 // kernels order these writes against their LDS reads with explicit
 // s_waitcnt vmcnt and workgroup barriers, and a compiler-inserted wait would
-// serialise the loads they deliberately keep in flight.
+// serialise the loads they deliberately keep in flight.  M0 is an input
+// operand ("{m0}"): the compiler writes it before the statement and knows it
+// holds that value, so nothing it generates can be disturbed by the load.
+// A direct load needs one wait state after M0 is written (the s_nop), which
+// the compiler cannot see inside the statement.
 __device__ __forceinline__ void load_lds_b128(i32x4 rsrc, HK_LDS void* lds_wave_base,
                                               uint32_t voffset, uint32_t soffset) {
     const uint32_t m0v = (uint32_t)(uintptr_t)lds_wave_base;
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
         :
-        : "s"(m0v), "v"(voffset), "s"(rsrc), "s"(soffset)
-        : "memory", "m0");
+        : "v"(voffset), "s"(rsrc), "s"(soffset), "{m0}"(m0v)
+        : "memory");
 }
 
 // The same direct load through the global path: lane i fetches 16 bytes at
@@ -71,12 +74,11 @@ __device__ __forceinline__ void load_lds_global_b128(const void* base, HK_LDS vo
                                                      uint32_t voffset) {
     const uint32_t m0v = (uint32_t)(uintptr_t)lds_wave_base;
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
+        "global_load_lds_dwordx4 %0, %1"
         :
-        : "s"(m0v), "v"(voffset), "s"(base)
-        : "memory", "m0");
+        : "v"(voffset), "s"(base), "{m0}"(m0v)
+        : "memory");
 }
 
 // ------------------------------------------------------------ MFMA wrappers
@@ -243,6 +245,42 @@ __device__ __forceinline__ uint32_t lane_id_here() {
     uint32_t l;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
     return l;
+}
+
+// Optional clock record of a launch: the first workgroup dealt to each of the
+// 8 chiplets (workgroups 0-7) writes the shader-clock counter (s_memtime,
+// which advances with the chiplet's clock) and the constant-rate counter
+// (s_memrealtime) at its start to stamps[4 * workgroup ..] and at its end to
+// stamps[4 * workgroup + 2 ..].  stamps == nullptr writes nothing.  The end's
+// address waits in an LDS slot, so no register holds it across the kernel.
+__device__ __forceinline__ uint64_t** clock_slot() {
+    __shared__ uint64_t* slot;
+    return &slot;
+}
+__device__ __forceinline__ void clock_stamp_begin(uint64_t* stamps) {
+    if (threadIdx.x == 0u) {
+        uint64_t* p = nullptr;
+        if (stamps != nullptr && blockIdx.x < 8u) {
+            p = stamps + 4u * blockIdx.x;
+            const uint64_t t = __builtin_amdgcn_s_memtime();
+            const uint64_t r = __builtin_amdgcn_s_memrealtime();
+            *reinterpret_cast<ulonglong2*>(p) = make_ulonglong2(t, r);
+            p += 2;
+        }
+        *clock_slot() = p;
+    }
+}
+// Called by every wave once its work (stores included) has completed; wave
+// is the wave's index in the workgroup.
+__device__ __forceinline__ void clock_stamp_end(uint32_t wave) {
+    if (wave == 0u && lane_id_here() == 0u) {
+        uint64_t* p = *clock_slot();
+        if (p != nullptr) {
+            const uint64_t t = __builtin_amdgcn_s_memtime();
+            const uint64_t r = __builtin_amdgcn_s_memrealtime();
+            *reinterpret_cast<ulonglong2*>(p) = make_ulonglong2(t, r);
+        }
+    }
 }
 
 // Swap between lane groups: rows of 16 lanes pair up as (0, 1) and (2, 3);

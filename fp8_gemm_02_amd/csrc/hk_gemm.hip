@@ -13,7 +13,7 @@
 #include "hk_gemm.h"
 #include "hk_kernels.hpp"
 
-#define HK_VERSION 100  // 0.1.0
+#define HK_VERSION 200  // 0.2.0
 
 // ------------------------------------------------------------------ kernels
 //
@@ -206,8 +206,7 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
         for (int32_t l : {opts->layout_a, opts->layout_b})
             if (l != HK_LAYOUT_K_CONTIGUOUS && l != HK_LAYOUT_K_STRIDED)
                 return HK_ERROR_INVALID_VALUE;
-        for (int i = 0; i < 2; ++i)
-            if (opts->reserved[i] != 0) return HK_ERROR_INVALID_VALUE;
+        if (!aligned(opts->clock_stamps, 16)) return HK_ERROR_INVALID_VALUE;
     }
     if (M == 0 || N == 0) return HK_SUCCESS;
     if (C == nullptr || ldc < N || !aligned(C, 2)) return HK_ERROR_INVALID_VALUE;
@@ -377,6 +376,7 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     g.ldsa = g.ldsb = 0;
     g.a_t = at;
     g.b_t = bt;
+    g.stamps = opts ? opts->clock_stamps : nullptr;
     g.c_align = (aligned(C, 16) && ldc % 8 == 0) ? 16
                 : (aligned(C, 8) && ldc % 4 == 0)  ? 8
                 : (aligned(C, 4) && ldc % 2 == 0)  ? 4
@@ -562,5 +562,15 @@ const char* hk_status_string(hk_status status) {
 }
 
 int32_t hk_version(void) { return HK_VERSION; }
+
+int32_t hk_wall_clock_khz(void) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    return khz;
+}
 
 }  // extern "C"

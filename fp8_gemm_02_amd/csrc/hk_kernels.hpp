@@ -52,6 +52,8 @@ struct GemmArgs {
     // operand stored transposed: A[k * lda + m], B[k * ldb + n] (basic kernel;
     // the 4-wave BF16 kernel takes the layout as template arguments)
     int32_t a_t, b_t;
+    // optional clock record (clock_stamp_begin); written by the 4-wave kernels only
+    uint64_t* stamps;
 };
 
 constexpr int kRowBytes = 128;  // bytes of K per stage in every tile row
@@ -385,6 +387,7 @@ __device__ __forceinline__ uint32_t rotated_stage(uint32_t s, uint32_t rot, uint
 template <bool kAT, bool kBT>
 __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf buf0,
                                               const IL4Buf buf1) {
+    clock_stamp_begin(g.stamps);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
@@ -638,6 +641,7 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         zero_acc();
     }
     wait_all();  // no LDS write may outlive the workgroup
+    clock_stamp_end(wave);
 }
 
 // FP8 form of the persistent 4-wave interleave: v_mfma_scale_f32_16x16x128_f8f6f4
@@ -701,6 +705,7 @@ template <bool kMx, bool kAT = false, bool kBT = false>
 __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf0,
                                              const IL4Buf buf1, HK_LDS uint8_t* scl) {
     static_assert(!(kMx && (kAT || kBT)), "block scales take K-contiguous operands only");
+    clock_stamp_begin(g.stamps);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t wm = wave >> 1;  // A rows wm*128 .. +127
@@ -1010,6 +1015,7 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         zero_acc();
     }
     wait_all();  // no LDS write may outlive the workgroup
+    clock_stamp_end(wave);
 }
 
 // ------------------------------------------------------- 8-wave interleave

@@ -139,7 +139,22 @@ typedef enum hk_layout {
     HK_LAYOUT_K_STRIDED = 1
 } hk_layout;
 
-/* Optional knobs for hk_gemm_ex.  Zero-initialise for the defaults. */
+/*
+ * Optional knobs for hk_gemm_ex.  Zero-initialise for the defaults.
+ *
+ * clock_stamps: NULL, or a caller-owned device buffer of 32 uint64_t (256
+ * bytes, 16-byte aligned; misaligned is HK_ERROR_INVALID_VALUE) that records
+ * the clocks of the launch.  The 4-wave kernels (INTERLEAVE4) write, for each
+ * of the first 8 workgroups x (the first workgroup dealt to chiplet x; the
+ * hardware deals workgroups to the 8 chiplets round-robin), the chiplet's
+ * shader-clock counter and the constant-rate counter as the workgroup starts
+ * (words 4x, 4x+1) and as it ends (words 4x+2, 4x+3).  The chiplet's mean
+ * clock over the launch is then (word 4x+2 - word 4x) / (word 4x+3 - word
+ * 4x+1) times the constant counter's rate, hk_wall_clock_khz().  Words of
+ * workgroups that do not exist, and the whole buffer under any other
+ * schedule, are left untouched.  The kernels and their results are the same
+ * with or without it.
+ */
 typedef struct hk_gemm_opts {
     int32_t schedule;    /* hk_schedule */
     int32_t grid_order;  /* hk_grid_order */
@@ -147,7 +162,7 @@ typedef struct hk_gemm_opts {
     int32_t window;      /* co-resident workgroups per window; 0 = CU count */
     int32_t layout_a;    /* hk_layout of A */
     int32_t layout_b;    /* hk_layout of B */
-    int32_t reserved[2]; /* must be zero */
+    uint64_t *clock_stamps; /* NULL, or 32 words of clock record (above) */
 } hk_gemm_opts;
 
 /* What a call with these arguments would launch (filled by hk_gemm_plan). */
@@ -229,6 +244,10 @@ hk_status hk_gemm_plan(int32_t dtype, const void *A, const void *B, const void *
 hk_status hk_grid_map(int32_t grid_order, int64_t tiles_m, int64_t tiles_n,
                       int32_t group_m, int32_t window, int32_t nxcd,
                       int64_t count, const int64_t *wg, int64_t *tm, int64_t *tn);
+
+/* Rate of the constant-rate counter the clock record uses (the current
+ * device's wall-clock rate attribute), in kHz; 0 if the runtime cannot say. */
+int32_t hk_wall_clock_khz(void);
 
 /* Static string for a status code ("HK_SUCCESS", ...). */
 const char *hk_status_string(hk_status status);

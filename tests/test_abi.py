@@ -37,7 +37,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-              "hk_grid_map", "hk_status_string", "hk_version", "hk_attn_fwd_bf16"):
+              "hk_grid_map", "hk_status_string", "hk_version", "hk_wall_clock_khz",
+              "hk_attn_fwd_bf16"):
         assert n in names
     assert set(names) == set(hk.EXPORTED)
 
@@ -53,7 +54,7 @@ def test_status_strings(L):
     assert hk.status_string(2) == "HK_ERROR_NOT_SUPPORTED"
     assert hk.status_string(3) == "HK_ERROR_LAUNCH"
     assert hk.status_string(99) == "HK_UNKNOWN_STATUS"
-    assert hk.hk_version() >= 100
+    assert hk.hk_version() >= 200
 
 
 BAD_BF16 = [
@@ -95,19 +96,32 @@ def test_ex_rejects_bad_dtype_and_options(L):
         st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
                           ctypes.byref(o), None)
         assert st == hk.HK_ERROR_INVALID_VALUE, field
-    o = hk.GemmOpts()
-    o.reserved[1] = 1
-    st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0, ctypes.byref(o), None)
-    assert st == hk.HK_ERROR_INVALID_VALUE
+    # the clock record takes 16-byte stores: a misaligned buffer is rejected
+    for off in (8, 4, 1):
+        o = hk.GemmOpts()
+        o.clock_stamps = FAKE + off
+        st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
+                          ctypes.byref(o), None)
+        assert st == hk.HK_ERROR_INVALID_VALUE, off
 
 
 def test_opts_struct_matches_the_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct hk_gemm_opts \{(.*?)\} hk_gemm_opts;", text, re.S).group(1)
-    fields = re.findall(r"int32_t (\w+)(?:\[(\d+)\])?;", body)
-    assert [(n, int(c or 1)) for n, c in fields] == [
-        (n, getattr(t, "_length_", 1)) for n, t in hk.GemmOpts._fields_]
+    fields = re.findall(r"(int32_t|uint64_t \*)\s*(\w+);", body)
+    ctype = {"int32_t": ctypes.c_int32, "uint64_t *": ctypes.c_void_p}
+    assert [(n, ctype[t]) for t, n in fields] == list(hk.GemmOpts._fields_)
     assert ctypes.sizeof(hk.GemmOpts) == 32
+    assert hk.GemmOpts.clock_stamps.offset == 24
+
+
+def test_chiplet_clocks_from_a_record():
+    # chiplet 0: 1.9e6 shader cycles over 1e5 ticks of a 100 MHz counter = 1.9 GHz;
+    # chiplet 1 recorded nothing
+    st = [0] * 32
+    st[0:4] = [10, 500, 10 + 1_900_000, 500 + 100_000]
+    got = hk.chiplet_clocks_ghz(st, 100_000)
+    assert abs(got[0] - 1.9) < 1e-12 and got[1] is None
 
 
 # Operand layouts: K_STRIDED stores A as K x M (lda >= M) and B as K x N (ldb >= N).

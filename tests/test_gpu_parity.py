@@ -454,3 +454,55 @@ def test_k_tail_probe_ragged():
     st = oracle.compare(got, ref, exact=True)
     assert st["ok"], st
     assert np.count_nonzero(ref) > 0.5 * ref.size  # the probe really exercises the tail
+
+
+# ---------------------------------------------------------------- clock record
+#
+# hk_gemm_opts.clock_stamps: the 4-wave kernels write, for workgroups 0-7, the
+# shader-clock and constant-rate counters at their start and end.  The record
+# must leave the product untouched and write nothing outside its 32 words.
+
+STAMP_SENTINEL = 0x5A5A5A5A5A5A5A5A
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_clock_record_leaves_results_unchanged(dtype):
+    M, N, K = 1024, 2048, 512  # 32 tiles: every chiplet gets a first workgroup
+    if dtype == "bf16":
+        A_cpu, B_cpu = _bf16(M, K, "int4", 71), _bf16(N, K, "int4", 72)
+        dt, sa, sb = hk.HK_DTYPE_BF16, 1.0, 1.0
+    else:
+        A_cpu = gemm_inputs.fp8_matrix(M, K, 73, integer=True)[0]
+        B_cpu = gemm_inputs.fp8_matrix(N, K, 74, integer=True)[0]
+        dt, sa, sb = hk.HK_DTYPE_FP8_E4M3, 0.5, 4.0
+    A, B = A_cpu.cuda(), B_cpu.cuda()
+    stamps = torch.full((40,), STAMP_SENTINEL, dtype=torch.int64, device="cuda")
+    plain = _run(dt, A, B, M, N, K, K, K, N, sa, sb, schedule="interleave4")
+    rec = _run(dt, A, B, M, N, K, K, K, N, sa, sb, schedule="interleave4", clock_stamps=stamps)
+    assert torch.equal(_as_i16(plain), _as_i16(rec))
+    st = stamps.cpu().tolist()
+    assert st[32:] == [STAMP_SENTINEL] * 8
+    ghz = hk.chiplet_clocks_ghz(st[:32], hk.hk_wall_clock_khz())
+    _say("clock record", dtype, [None if g is None else round(g, 3) for g in ghz])
+    for x in range(8):
+        t0, r0, t1, r1 = st[4 * x:4 * x + 4]
+        assert STAMP_SENTINEL not in (t0, r0, t1, r1) and t1 > t0 and r1 > r0, (x, st)
+        assert 0.3 < ghz[x] < 3.5, ghz
+
+
+def _as_i16(C):
+    return C.view(torch.int16)
+
+
+def test_clock_record_untouched_without_those_workgroups_or_schedule():
+    # two tiles: only workgroups 0 and 1 exist; BASIC never writes the record
+    M, N, K = 256, 512, 256
+    A, B = _bf16(M, K, "int4", 75).cuda(), _bf16(N, K, "int4", 76).cuda()
+    stamps = torch.full((32,), STAMP_SENTINEL, dtype=torch.int64, device="cuda")
+    _run(hk.HK_DTYPE_BF16, A, B, M, N, K, K, K, N, schedule="interleave4", clock_stamps=stamps)
+    st = stamps.cpu().tolist()
+    assert STAMP_SENTINEL not in st[:8]
+    assert st[8:] == [STAMP_SENTINEL] * 24
+    stamps.fill_(STAMP_SENTINEL)
+    _run(hk.HK_DTYPE_BF16, A, B, M, N, K, K, K, N, schedule="basic", clock_stamps=stamps)
+    assert stamps.cpu().tolist() == [STAMP_SENTINEL] * 32
