@@ -8,8 +8,10 @@ Each pin checks the oracle against something other than itself:
 * 50-digit mpmath softmax attention on tiny inputs, rounded to bf16 by exact
   rational comparison: the oracle's bf16 output must be the correctly rounded
   exact value;
-* closed forms: all-zero queries give the mean of the visible value rows and
-  LSE = log(n); a single key gives that key's value row exactly; the first
+* closed forms: all-zero queries give the mean of the visible value rows,
+  LSE = log(n) and a tolerance magnitude A equal to the mean of the visible
+  values' magnitudes (A is also checked against torch's float64 softmax
+  weights applied to |V|); a single key gives that key's value row exactly; the first
   causal row sees only key 0; a key that dominates by more than the double
   exponent range gives its value row exactly; a hand-derived mean that single
   rounding and double rounding (through float) round differently;
@@ -52,7 +54,7 @@ def test_matches_torch_sdpa_float64(oracle_mod, B, Hq, Hkv, N, D, causal):
     k = _bf16((B, Hkv, N, D), 2 + N)
     v = _bf16((B, Hkv, N, D), 3 + N)
     scale = D ** -0.5
-    o, o64, lse, _ = _run(oracle_mod, q, k, v, scale, causal)
+    o, o64, lse, amag = _run(oracle_mod, q, k, v, scale, causal)
     rep = Hq // Hkv
     kd = k.double().repeat_interleave(rep, dim=1)
     vd = v.double().repeat_interleave(rep, dim=1)
@@ -63,6 +65,11 @@ def test_matches_torch_sdpa_float64(oracle_mod, B, Hq, Hkv, N, D, causal):
     if causal:
         s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
     assert np.abs(lse - torch.logsumexp(s, dim=-1).reshape(-1).numpy()).max() <= 1e-12
+    # the tolerance magnitude A = sum_j p_j |v_j| / sum_j p_j: torch's float64
+    # softmax weights applied to |V| (an independent computation of the same
+    # weighted mean of magnitudes)
+    a_ref = torch.softmax(s, dim=-1) @ vd.abs()
+    assert np.abs(amag - a_ref.reshape(-1, D).numpy()).max() <= 1e-13
 
 
 def _mp_attention(q, k, v, scale, causal, dps=50):
@@ -119,7 +126,7 @@ def test_zero_queries_give_the_mean_of_visible_values(oracle_mod, causal):
     q = torch.zeros(B, H, N, D, dtype=torch.bfloat16)
     k = _bf16((B, H, N, D), 7)
     v = _bf16((B, H, N, D), 8)
-    o, _, lse, _ = _run(oracle_mod, q, k, v, 0.3, causal)
+    o, _, lse, amag = _run(oracle_mod, q, k, v, 0.3, causal)
     vv = v.double().numpy()
     for h in range(H):
         for i in range(N):
@@ -129,6 +136,9 @@ def test_zero_queries_give_the_mean_of_visible_values(oracle_mod, causal):
             for d in range(D):
                 mean = sum(Fraction(float(vv[0, h, j, d])) for j in range(n)) / n
                 assert int(o[r, d]) == _fraction_to_bf16_bits(mean), (h, i, d)
+                # equal weights: A is the mean magnitude of the visible values
+                amean = sum(abs(Fraction(float(vv[0, h, j, d]))) for j in range(n)) / n
+                assert abs(Fraction(float(amag[r, d])) - amean) <= amean * Fraction(1, 2 ** 50)
 
 
 def test_mean_that_double_rounding_gets_wrong(oracle_mod):

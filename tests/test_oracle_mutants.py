@@ -8,7 +8,8 @@ scale bias, swapped scale arrays, a NaN scale read as finite, an ignored scale
 stride; for attention: a dropped scale, a causal mask that is off by one or
 missing, the wrong grouped-query head, no max shift, no log in the LSE, keys
 read as values, a dropped last key, rounding through float, an ignored head
-stride), builds the copy on the CPU in a temporary directory, and
+stride, a tolerance magnitude that is not normalised or not taken of |v|),
+builds the copy on the CPU in a temporary directory, and
 runs the pins of test_oracle.py, test_oracle_mx.py and test_oracle_attn.py
 against it.  At least one pin must fail for
 every mutant.  The oracle itself is never modified.
@@ -57,6 +58,8 @@ MUTANTS = {
     "attn_rounded_through_float": ("o[d] = oracle_bf16_round(val);",
                                    "o[d] = oracle_bf16_round((double)(float)val);"),
     "attn_ignored_head_stride": ("h * sq[1]", "h * D"),
+    "attn_amag_unnormalised": ("amag[d] = mag / l;", "amag[d] = mag;"),
+    "attn_amag_signed": ("mag += s[j] * fabs(v);", "mag += s[j] * v;"),
 }
 
 PINS = [
