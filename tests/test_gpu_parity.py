@@ -506,3 +506,108 @@ def test_clock_record_untouched_without_those_workgroups_or_schedule():
     stamps.fill_(STAMP_SENTINEL)
     _run(hk.HK_DTYPE_BF16, A, B, M, N, K, K, K, N, schedule="basic", clock_stamps=stamps)
     assert stamps.cpu().tolist() == [STAMP_SENTINEL] * 32
+
+
+# ------------------------------------------------------- full-size, compared in full
+#
+# 4096^3 costs the oracle about 15 s on 16 host threads, so it is compared
+# element by element, random and integer-valued, in the launch configuration
+# the benchmark times.  At 8192^3 whole 256-row tile bands (the first, an
+# interior one chosen by seed, and the last) are compared against the oracle.
+# Integer-valued inputs have one exact product whatever the summation order
+# (every partial sum is an integer far below 2^53), so at 8192^3 and on the
+# MLP shape every output element is also checked bit for bit against a
+# float64 product of the same integers, rounded once to bf16 (on the ragged
+# shape too, where every edge tile and the K tail of 8 take part).
+
+def _launch_default(w, x, sa=None, sb=None, **opts):
+    M, N, K = w.M, w.N, w.K
+    A, B = x["A"].cuda(), x["B"].cuda()
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    sa = x["scale_a"] if sa is None else sa
+    sb = x["scale_b"] if sb is None else sb
+    _say("launch", w.name, (M, N, K), opts or "bench launch configuration")
+    if opts:
+        dt = hk.HK_DTYPE_BF16 if w.dtype == "bf16" else hk.HK_DTYPE_FP8_E4M3
+        hk.hk_gemm_ex(dt, A, B, C, M, N, K, K, K, N, sa, sb, **opts)
+    elif w.dtype == "bf16":
+        hk.hk_gemm_bf16(A, B, C, M, N, K, K, K, N)
+    else:
+        hk.hk_gemm_fp8(A, B, C, M, N, K, K, K, N, sa, sb)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_bf16_4096_compared_in_full(integer):
+    w = gemm_inputs.WORKLOADS["bf16_4096"]
+    x = gemm_inputs.make_inputs(w, integer=integer)
+    C = _launch_default(w, x)
+    got = _bits16(C)
+    ref, S = oracle.gemm("bf16", gemm_inputs.bits(x["A"]).ravel(), gemm_inputs.bits(x["B"]).ravel(),
+                         w.M, w.N, w.K)
+    st = oracle.compare(got, ref, S, exact=integer, rel_tol=RTOL)
+    _say("bf16_4096 full", "integer" if integer else w.dist,
+         {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
+
+
+def _tile_bands(M, rng):
+    interior = int(rng.integers(1, M // 256 - 1)) * 256
+    return [0, interior, M - 256]
+
+
+@pytest.mark.parametrize("schedule", [None, "pingpong8"])
+def test_bf16_8192_tile_bands_against_the_oracle(schedule):
+    w = gemm_inputs.WORKLOADS["bf16_8192"]
+    x = gemm_inputs.make_inputs(w)
+    C = _launch_default(w, x, **({"schedule": schedule} if schedule else {}))
+    Ab, Bb = gemm_inputs.bits(x["A"]), gemm_inputs.bits(x["B"])
+    for r0 in _tile_bands(w.M, np.random.default_rng(11)):
+        ref, S = oracle.gemm("bf16", np.ascontiguousarray(Ab[r0:r0 + 256]).ravel(), Bb.ravel(),
+                             256, w.N, w.K)
+        st = oracle.compare(_bits16(C[r0:r0 + 256]), ref, S, rel_tol=RTOL)
+        _say("bf16_8192", schedule or "default", "rows", r0, r0 + 255,
+             {k: st[k] for k in st if k != "ulp_hist"})
+        assert st["ok"], (r0, st)
+
+
+def _exact_integer_product(A_cpu, B_cpu, scale=1.0):
+    """bf16 bits of scale * A B^T for integer-valued operands, computed exactly."""
+    a = A_cpu.to(torch.float64) if A_cpu.dtype == torch.bfloat16 else \
+        torch.from_numpy(oracle.e4m3_table()[gemm_inputs.bits(A_cpu)])
+    b = B_cpu.to(torch.float64) if B_cpu.dtype == torch.bfloat16 else \
+        torch.from_numpy(oracle.e4m3_table()[gemm_inputs.bits(B_cpu)])
+    prod = (a @ b.t()) * scale
+    assert float(prod.abs().max()) < 2.0 ** 24  # every sum is exact in fp32 too
+    return oracle.bf16_round(prod.numpy())
+
+
+@pytest.mark.parametrize("name,schedule", [("bf16_8192", None), ("bf16_8192", "pingpong8"),
+                                           ("bf16_mlp", None), ("bf16_mlp_ragged", None),
+                                           ("fp8_8192", None)])
+def test_full_size_integer_exact_everywhere(name, schedule):
+    w = gemm_inputs.WORKLOADS[name]
+    x = gemm_inputs.make_inputs(w, integer=True)
+    sa, sb = (0.5, 4.0) if w.dtype == "fp8" else (1.0, 1.0)
+    C = _launch_default(w, x, sa, sb, **({"schedule": schedule} if schedule else {}))
+    want = _exact_integer_product(x["A"], x["B"], sa * sb)
+    got = _bits16(C)
+    same = (got == want) | (((got | want) & 0x7FFF) == 0)  # +0 and -0 are equal
+    bad = int((~same).sum())
+    _say(name, schedule or "default", "integer-valued, every element exact:", bad == 0, bad)
+    assert bad == 0
+
+
+def test_pingpong8_8192_sampled():
+    w = gemm_inputs.WORKLOADS["bf16_8192"]
+    x = gemm_inputs.make_inputs(w)
+    C = _launch_default(w, x, schedule="pingpong8")
+    rng = np.random.default_rng(13)
+    rows, cols = _edge_samples(w.M, w.N, 256, rng, 3000)
+    got = _bits16(C[torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()])
+    ref, S = oracle.gemm_sampled("bf16", gemm_inputs.bits(x["A"]).ravel(),
+                                 gemm_inputs.bits(x["B"]).ravel(), w.M, w.N, w.K, rows, cols)
+    st = oracle.compare(got, ref, S, rel_tol=RTOL)
+    _say("bf16_8192 pingpong8 sampled", rows.size, {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
