@@ -22,7 +22,7 @@ C ABI) on inputs already resident in HBM.  Order of a run:
      and by one pair of HIP events on the launch stream, launched as soon as
      the queue has drained, with every argument built beforehand; `value` is
      2*M*N*K*K / wall time, `roofline.achieved` uses the event time / K.
-     The 4-wave kernels record their clocks in every timed launch
+     The persistent kernels record their clocks in every timed launch
      (hk_gemm_opts.clock_stamps, which costs nothing measurable): `clock_ghz`.
   4. K more launches, each bracketed by its own events (per-launch events
      cost about 5 us of gap per launch, so they stay out of the timed
@@ -412,9 +412,10 @@ def main():
             hk.hk_gemm_ex(dtype_code, A, B, C, w.M, w.N, w.K, w.lda, w.ldb, w.N, sa, sb,
                           stream=stream, clock_stamps=stamps, **opts)
 
-    # the 4-wave kernels write a clock record per launch (32 words each)
+    # the persistent kernels write a clock record per launch (32 words each)
     stamps = (torch.zeros((a.steps, 32), dtype=torch.int64, device=dev)
-              if w.dtype != "mxfp8" and plan["schedule"] == hk.HK_SCHEDULE_INTERLEAVE4 else None)
+              if w.dtype != "mxfp8" and plan["schedule"] in (hk.HK_SCHEDULE_INTERLEAVE4,
+                                                              hk.HK_SCHEDULE_PINGPONG8) else None)
     print("[bench] settle, %d warm-up steps, %d timed" % (a.warmup, a.steps), file=sys.stderr,
           flush=True)
     torch.cuda.synchronize()

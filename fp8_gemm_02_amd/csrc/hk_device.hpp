@@ -293,23 +293,25 @@ __device__ __forceinline__ void swap_row_pairs(uint32_t& x, uint32_t& y) {
 }
 
 // Store one 16-row block of a wave's C sub-tile.  Lane (r, g) (r = lane % 16,
-// g = lane / 16) holds, for blocks j = 0..7, C[m][c0 + 16j + 4g .. +3] in
+// g = lane / 16) holds, for blocks j = 0..kNB-1, C[m][c0 + 16j + 4g .. +3] in
 // a[j] (times s); m is the lane's row, ok whether it lies inside C.  With
 // 16-byte aligned 8-column groups (align 16) each pair of blocks (j, j+1)
 // goes out as one 16-byte store per lane: lane groups g and g+1 trade their
 // halves (swap_row_pairs), so that even groups hold columns
 // c0 + 16j + 4g .. +7 and odd groups c0 + 16(j+1) + 4(g-1) .. +7.  Half the
 // store instructions of 8-byte stores, each covering 64 bytes of a row.
+template <int kNB>
 __device__ __forceinline__ void store_c_rows(uint16_t* crow, bool ok, int32_t c0, uint32_t g,
-                                             int32_t N, const f32x4 (&a)[8], float s,
+                                             int32_t N, const f32x4 (&a)[kNB], float s,
                                              int32_t align) {
+    static_assert(kNB % 2 == 0, "blocks are stored in pairs");
     // an opaque copy of the lane group: the column offsets below are then
     // computed here, not hoisted out of the tile loop and kept live (spilled)
     // across it
     asm volatile("" : "+v"(g));
     if (align >= 16) {
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
+        for (int j = 0; j < kNB; j += 2) {
             const f32x4 u = a[j] * s, v = a[j + 1] * s;
             uint32_t x0 = pack_bf16x2(u.x, u.y), x1 = pack_bf16x2(u.z, u.w);
             uint32_t y0 = pack_bf16x2(v.x, v.y), y1 = pack_bf16x2(v.z, v.w);
@@ -328,7 +330,7 @@ __device__ __forceinline__ void store_c_rows(uint16_t* crow, bool ok, int32_t c0
         }
     } else if (ok) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kNB; ++j) {
             const int32_t n = c0 + 16 * j + 4 * (int32_t)g;
             if (n < N) store_bf16x4(crow + n, n, N, a[j] * s, align);
         }

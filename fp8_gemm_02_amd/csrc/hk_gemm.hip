@@ -358,8 +358,9 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     if (p->tiles_m * p->tiles_n > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
 
     p->grid = p->tiles_m * p->tiles_n;
-    // the 4-wave kernels are persistent: one workgroup per compute unit
-    if (sched == HK_SCHEDULE_INTERLEAVE4 && p->grid > cus) p->grid = cus;
+    // the 4-wave and ping-pong kernels are persistent: one workgroup per compute unit
+    if ((sched == HK_SCHEDULE_INTERLEAVE4 || sched == HK_SCHEDULE_PINGPONG8) && p->grid > cus)
+        p->grid = cus;
     hk::GemmArgs& g = p->args;
     g.A = (const uint8_t*)A;
     g.B = (const uint8_t*)B;

@@ -52,7 +52,7 @@ struct GemmArgs {
     // operand stored transposed: A[k * lda + m], B[k * ldb + n] (basic kernel;
     // the 4-wave BF16 kernel takes the layout as template arguments)
     int32_t a_t, b_t;
-    // optional clock record (clock_stamp_begin); written by the 4-wave kernels only
+    // optional clock record (clock_stamp_begin); written by the persistent kernels only
     uint64_t* stamps;
 };
 
@@ -89,8 +89,33 @@ struct PP8Buf {
     HK_LDS i32x4* b;    // B tile rows 0-255 (32 KiB)
 };
 
+// Chiplet-rotated K order of the persistent kernels.  All CUs walk
+// the K stages of their tiles in lockstep, and the 8 chiplets share each
+// A (or B) panel of a window: with one K order, all 8 L2s miss on the same
+// lines at the same moment and queue at the last-level cache (fabric read
+// latency about 1.5 times hipBLASLt's, measured with TCC_EA0_RDREQ_LEVEL).
+// Chiplet x (workgroup w runs on chiplet w mod 8) starts its tiles' whole
+// stages x/8 of the way into K and wraps around; the CUs of one chiplet keep
+// one order, so their L2 sharing is untouched.  The partial last stage and
+// the stages past K keep their places.  Only the order of the fp32 sums
+// changes.
+__device__ __forceinline__ uint32_t chiplet_k_rotation(uint32_t nk_whole) {
+    return ((blockIdx.x & 7u) * nk_whole) >> 3;
+}
+__device__ __forceinline__ uint32_t rotated_stage(uint32_t s, uint32_t rot, uint32_t nk_whole) {
+    if (s >= nk_whole) return s;
+    const uint32_t r = s + rot;
+    return r >= nk_whole ? r - nk_whole : r;
+}
+
+// Persistent like the 4-wave kernels: one workgroup per compute unit walks
+// tiles w = b, b + G, ... (G = grid size), and the stage pipeline runs
+// through tile boundaries (stages past a tile's last one are the next
+// tile's first), with the chiplet-rotated K order, global direct loads for
+// the whole stages of tiles inside C and 16-byte C stores.
 template <bool kFp8, int kSwz>
 __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, const PP8Buf buf1) {
+    clock_stamp_begin(g.stamps);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // Group 0 (waves 0-3) owns output rows 0..127 of the tile and issues all
@@ -98,13 +123,12 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
     // wave wq owns the 64-column strip wq.
     const uint32_t grp = wave >> 2;
     const uint32_t wq = wave & 3u;
-
-    uint32_t tm, tn;
-    tile_of(blockIdx.x, g.grid, &tm, &tn);
-    const int32_t m0 = (int32_t)tm * kPP8Tile;
-    const int32_t n0 = (int32_t)tn * kPP8Tile;
+    const uint32_t total = (uint32_t)g.grid.tiles_m * (uint32_t)g.grid.tiles_n;
     const uint32_t kbytes = (uint32_t)g.K * (kFp8 ? 1u : 2u);
     const uint32_t nk = (kbytes + kRowBytes - 1) / kRowBytes;
+    const uint32_t nk_pad = (nk + 1u) & ~1u;  // stages run in pairs
+    const uint32_t nk_whole = kbytes / kRowBytes;
+    const uint32_t krot = chiplet_k_rotation(nk_whole);
 
     // ---- HBM -> LDS.  A stage of an operand is 32 blocks of 8 rows; one
     // 16-byte load per lane moves a block (lane l -> row 8b + l/8, physical
@@ -114,19 +138,10 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
     // each region as soon as it is free:
     //   batch HI(s): A-hi of stage s       (4 loads per wave), one stage ahead
     //   batch LO(s): B and A-lo of stage s (12 loads per wave), two stages ahead
-    // so every batch has six phases to land.  Batches for stages past the end
-    // are issued anyway with every lane out of range (they only write zeros
-    // into regions nobody reads again), which keeps every wait count constant.
+    // so every batch has six phases to land.  Stages past a tile's K (the
+    // pad stage and the ones past the last tile) read zeros, which keeps
+    // every wait count constant.
     const uint32_t kc_lane = (lane & 7u) ^ swz_key<kSwz>(wq * 8u + (lane >> 3));
-    uint32_t span_a = 0, span_b = 0;
-    {
-        const uint64_t sa = (uint64_t)(g.M - m0) * g.lda_b;  // rows past the edge read as zero
-        const uint64_t sb = (uint64_t)(g.N - n0) * g.ldb_b;
-        span_a = (uint32_t)(sa > kOobOffset ? kOobOffset : sa);
-        span_b = (uint32_t)(sb > kOobOffset ? kOobOffset : sb);
-    }
-    const i32x4 rsrc_a = make_rsrc_words(g.A + (int64_t)m0 * g.lda_b, span_a);
-    const i32x4 rsrc_b = make_rsrc_words(g.B + (int64_t)n0 * g.ldb_b, span_b);
     const uint32_t vrow_a = (lane >> 3) * g.lda_b + kc_lane * 16u;
     const uint32_t vrow_b = (lane >> 3) * g.ldb_b + kc_lane * 16u;
     // This wave's blocks: region block r = wq + 4j.  In A-lo, region blocks
@@ -143,27 +158,56 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
 #pragma unroll
     for (int j = 0; j < 8; ++j) vlo_b[j] = vrow_b + (wq + 4u * j) * 8u * g.ldb_b;
 
-    // One load of region block `block`.  Masked: lanes whose chunk is at or
-    // past K (or any lane, for a stage past the end) read zero; the main loop,
-    // whose stages all lie inside K, skips that select.
-    auto ld = [&](auto masked, const i32x4& rs, HK_LDS i32x4* dst, uint32_t block,
-                  uint32_t voff, uint32_t s) {
+    // Buffer resources of a tile's A and B row panels; rows past the matrix
+    // edge read as zero, and a tile past the end gets empty resources.
+    struct Tile {
+        i32x4 ra, rb;
+        int32_t m0, n0;
+    };
+    auto tile = [&](uint32_t w) {
+        Tile t;
+        uint32_t tm = 0, tn = 0;
+        if (w < total) tile_of(w, g.grid, &tm, &tn);
+        t.m0 = (int32_t)tm * kPP8Tile;
+        t.n0 = (int32_t)tn * kPP8Tile;
+        const uint64_t sa = w < total ? (uint64_t)(g.M - t.m0) * g.lda_b : 0;
+        const uint64_t sb = w < total ? (uint64_t)(g.N - t.n0) * g.ldb_b : 0;
+        t.ra = make_rsrc_words(g.A + (int64_t)t.m0 * g.lda_b,
+                               (uint32_t)(sa > kOobOffset ? kOobOffset : sa));
+        t.rb = make_rsrc_words(g.B + (int64_t)t.n0 * g.ldb_b,
+                               (uint32_t)(sb > kOobOffset ? kOobOffset : sb));
+        return t;
+    };
+
+    // One load of region block `block` of stage s0 of tile tt.  Masked: lanes
+    // whose chunk is at or past K (every lane, for a stage past the end) read
+    // zero.  glob: the tile lies inside C and the stage inside K, so the
+    // unchecked global form reads only the operand.
+    auto ld = [&](auto masked, auto glob, const Tile& tt, bool is_a, HK_LDS i32x4* dst,
+                  uint32_t block, uint32_t voff, uint32_t s0) {
+        const uint32_t s = rotated_stage(s0, krot, nk_whole);
+        const uint32_t koff = s * (uint32_t)kRowBytes;
+        if constexpr (decltype(glob)::value) {
+            const uint8_t* base = is_a ? g.A + (int64_t)tt.m0 * g.lda_b + koff
+                                       : g.B + (int64_t)tt.n0 * g.ldb_b + koff;
+            load_lds_global_b128(base, (HK_LDS void*)(dst + block * 64u), voff);
+            return;
+        }
         // the stage offset rides in the (uniform) scalar offset; a masked lane's
         // vector offset alone already lies past the end of the buffer
-        const uint32_t koff = s * (uint32_t)kRowBytes;
         if constexpr (decltype(masked)::value)
             voff = koff + kc_lane * 16u < kbytes ? voff : kOobOffset;
-        load_lds_b128(rs, (HK_LDS void*)(dst + block * 64u), voff, koff);
+        load_lds_b128(is_a ? tt.ra : tt.rb, (HK_LDS void*)(dst + block * 64u), voff, koff);
     };
-    auto issue_hi = [&](auto masked, const PP8Buf& d, uint32_t s) {
+    auto issue_hi = [&](auto masked, auto glob, const Tile& tt, const PP8Buf& d, uint32_t s) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ld(masked, rsrc_a, d.ahi, wq + 4u * j, vhi[j], s);
+        for (int j = 0; j < 4; ++j) ld(masked, glob, tt, true, d.ahi, wq + 4u * j, vhi[j], s);
     };
-    auto issue_lo = [&](auto masked, const PP8Buf& d, uint32_t s) {
+    auto issue_lo = [&](auto masked, auto glob, const Tile& tt, const PP8Buf& d, uint32_t s) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ld(masked, rsrc_b, d.b, wq + 4u * j, vlo_b[j], s);
+        for (int j = 0; j < 8; ++j) ld(masked, glob, tt, false, d.b, wq + 4u * j, vlo_b[j], s);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ld(masked, rsrc_a, d.alo, wq + 4u * j, vlo_a[j], s);
+        for (int j = 0; j < 4; ++j) ld(masked, glob, tt, true, d.alo, wq + 4u * j, vlo_a[j], s);
     };
 
     // ---- LDS -> register fragments.  Fragment rows start at multiples of 16,
@@ -178,10 +222,12 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
     const uint32_t fb1 = (wq * 64u + r16) * kChunks + ((4u + g4) ^ key);
 
     f32x4 acc[8][4];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
     // A fragment is the lane's two 16-byte chunks of one row block: K chunks
     // g and g+4 of the stage.  BF16 feeds them to two 16x16x32 MFMAs (one
     // K slice each); FP8 feeds the pair to one 16x16x128 MFMA.
@@ -215,8 +261,11 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
     // M1 C1 M2 C2, group 1 runs the same one phase later, so in every phase
     // one group issues memory work while the other issues matrix-core work.
     // cur holds stage t; oth holds stage t+1 (or is being filled with it).
+    // The loader sends HI of stage sh of tile th and LO of stage sl of tile tl
+    // (the next stage and the one after, possibly of the next tile).
     const bool loader = (grp == 0);
-    auto stage = [&](auto masked, const PP8Buf& cur, const PP8Buf& oth, uint32_t t) {
+    auto stage = [&](auto masked, auto glob, const PP8Buf& cur, const PP8Buf& oth,
+                     const Tile& th, uint32_t sh, const Tile& tl, uint32_t sl) {
         i32x8 af[4], bfr[4];
         // M1: A-lo fragments (row blocks 0-3) and all B fragments of stage t;
         // the loader sends HI(t+1) into the other buffer, whose A-hi was last
@@ -225,7 +274,7 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         for (int mb = 0; mb < 4; ++mb) af[mb] = frag(cur.alo, fa0 + mb * 128, fa1 + mb * 128);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) bfr[nb] = frag(cur.b, fb0 + nb * 128, fb1 + nb * 128);
-        if (loader) issue_hi(masked, oth, t + 1);
+        if (loader) issue_hi(masked, glob, th, oth, sh);
         wait_lgkmcnt0();
         fenced_barrier();
         // C1; then HI(t) must have landed (newer in flight: LO(t+1), HI(t+1))
@@ -239,7 +288,7 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         // this buffer's B and A-lo, so the loader sends LO(t+2) into them
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) af[mb] = frag(cur.ahi, fa0 + mb * 128, fa1 + mb * 128);
-        if (loader) issue_lo(masked, cur, t + 2);
+        if (loader) issue_lo(masked, glob, tl, cur, sl);
         wait_lgkmcnt0();
         fenced_barrier();
         // C2; then LO(t+1) must have landed (newer in flight: HI(t+1), LO(t+2))
@@ -251,51 +300,77 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         fenced_barrier();
     };
 
-    // prologue: LO(0), HI(0), LO(1) in flight; LO(0) must have landed
+    // prologue: LO(0), HI(0), LO(1) of the first tile in flight; LO(0) must
+    // have landed
     const std::true_type masked;
     const std::false_type unmasked;
+    const std::false_type checked;
+    const std::true_type unchecked;
+    uint32_t w = blockIdx.x;
+    Tile cur = tile(w);
     if (loader) {
-        issue_lo(masked, buf0, 0);
-        issue_hi(masked, buf0, 0);
-        issue_lo(masked, buf1, 1);
+        issue_lo(masked, checked, cur, buf0, 0);
+        issue_hi(masked, checked, cur, buf0, 0);
+        issue_lo(masked, checked, cur, buf1, 1);
         wait_vmcnt<16>();
     }
     fenced_barrier();
     if (grp == 1) fenced_barrier();  // start group 1 one phase behind
-    // Stage pair (t, t+1) loads up to stage t+3, all inside K while
-    // t + 4 <= the number of whole stages.
-    const uint32_t nk_whole = kbytes / kRowBytes;
-    uint32_t t = 0;
-    for (; t + 4 <= nk_whole; t += 2) {
-        stage(unmasked, buf0, buf1, t);
-        stage(unmasked, buf1, buf0, t + 1);
-    }
-    for (; t < nk; t += 2) {
-        stage(masked, buf0, buf1, t);
-        if (t + 1 < nk) stage(masked, buf1, buf0, t + 1);
-    }
-    if (grp == 0) fenced_barrier();  // match group 1's barrier count
-    wait_vmcnt0();                   // no LDS write may outlive the workgroup
+    zero_acc();
 
-    // ---- epilogue: lane holds C[m][n..n+3] for each (mb, nb)
-    const int32_t mrow = m0 + (int32_t)(grp * 128u + r16);
-    const int32_t ncol = n0 + (int32_t)(wq * 64u + g4 * 4u);
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-        const int32_t m = mrow + mb * 16;
-        if (m < g.M) {
-            uint16_t* crow = g.C + (int64_t)m * g.ldc;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                const int32_t n = ncol + nb * 16;
-                if (n < g.N) {
-                    f32x4 v = acc[mb][nb];
-                    if constexpr (kFp8) v *= g.scale;
-                    store_bf16x4(crow + n, n, g.N, v, g.c_align);
-                }
+    for (;;) {
+        const uint32_t w_next = w + gridDim.x;
+        const Tile nxt = tile(w_next);
+        // Stage pair (t, t+1) loads up to stage t+3, all whole stages of this
+        // tile while t + 4 <= nk_whole.
+        uint32_t t = 0;
+        const bool inside = cur.m0 + kPP8Tile <= g.M && cur.n0 + kPP8Tile <= g.N;
+        if (inside) {
+            for (; t + 4 <= nk_whole; t += 2) {
+                stage(unmasked, unchecked, buf0, buf1, cur, t + 1, cur, t + 2);
+                stage(unmasked, unchecked, buf1, buf0, cur, t + 2, cur, t + 3);
+            }
+        } else {
+            for (; t + 4 <= nk_whole; t += 2) {
+                stage(unmasked, checked, buf0, buf1, cur, t + 1, cur, t + 2);
+                stage(unmasked, checked, buf1, buf0, cur, t + 2, cur, t + 3);
             }
         }
+        // the last pairs: stages at or past the end of this tile's K are the
+        // next tile's first (stage s of this tile is stage s - nk_pad of the next)
+        auto pick = [&](uint32_t s, uint32_t* s_out) -> const Tile& {
+            const bool mine = s < nk_pad;
+            *s_out = mine ? s : s - nk_pad;
+            return mine ? cur : nxt;
+        };
+        for (; t < nk_pad; t += 2) {
+            uint32_t h0, l0, h1, l1;
+            const Tile& th0 = pick(t + 1, &h0);
+            const Tile& tl0 = pick(t + 2, &l0);
+            stage(masked, checked, buf0, buf1, th0, h0, tl0, l0);
+            const Tile& th1 = pick(t + 2, &h1);
+            const Tile& tl1 = pick(t + 3, &l1);
+            stage(masked, checked, buf1, buf0, th1, h1, tl1, l1);
+        }
+
+        // ---- epilogue, at the start of this group's next memory phase: lane
+        // holds C[m][n..n+3] for each (mb, nb)
+        const uint32_t le = lane_id_here();
+        const int32_t mrow = cur.m0 + (int32_t)(grp * 128u + (le & 15u));
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const int32_t m = mrow + mb * 16;
+            store_c_rows(g.C + (int64_t)m * g.ldc, m < g.M, cur.n0 + (int32_t)(wq * 64u), le >> 4,
+                         g.N, acc[mb], kFp8 ? g.scale : 1.0f, g.c_align);
+        }
+        if (w_next >= total) break;
+        w = w_next;
+        cur = nxt;
+        zero_acc();
     }
+    if (grp == 0) fenced_barrier();  // match group 1's barrier count
+    wait_all();                      // no LDS write may outlive the workgroup
+    clock_stamp_end(wave);
 }
 
 // ------------------------------------------------------- 4-wave interleave
@@ -364,25 +439,6 @@ __device__ __forceinline__ uint32_t km_key(uint32_t k) {
 }
 constexpr uint32_t kKMRowBytes = kIL4Tile * 2u;    // one K-row of a transposed stage image
 constexpr uint32_t kKMStageRows = kRowBytes / 2u;  // 64 K-rows of bf16 per stage
-
-// Chiplet-rotated K order of the persistent 4-wave kernels.  All CUs walk
-// the K stages of their tiles in lockstep, and the 8 chiplets share each
-// A (or B) panel of a window: with one K order, all 8 L2s miss on the same
-// lines at the same moment and queue at the last-level cache (fabric read
-// latency about 1.5 times hipBLASLt's, measured with TCC_EA0_RDREQ_LEVEL).
-// Chiplet x (workgroup w runs on chiplet w mod 8) starts its tiles' whole
-// stages x/8 of the way into K and wraps around; the CUs of one chiplet keep
-// one order, so their L2 sharing is untouched.  The partial last stage and
-// the stages past K keep their places.  Only the order of the fp32 sums
-// changes.
-__device__ __forceinline__ uint32_t chiplet_k_rotation(uint32_t nk_whole) {
-    return ((blockIdx.x & 7u) * nk_whole) >> 3;
-}
-__device__ __forceinline__ uint32_t rotated_stage(uint32_t s, uint32_t rot, uint32_t nk_whole) {
-    if (s >= nk_whole) return s;
-    const uint32_t r = s + rot;
-    return r >= nk_whole ? r - nk_whole : r;
-}
 
 template <bool kAT, bool kBT>
 __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf buf0,

@@ -70,7 +70,8 @@ typedef enum hk_dtype {
  * scheduling: wave patterns"):
  *   PINGPONG8   8 waves per CU in two groups of four; while one group issues
  *               its matrix-core cluster the other issues its memory cluster,
- *               and they swap at workgroup barriers;
+ *               and they swap at workgroup barriers; persistent like
+ *               INTERLEAVE4;
  *   INTERLEAVE4 4 waves per CU, each interleaving its own loads with its
  *               matrix-core instructions; persistent (one workgroup per CU
  *               walks its share of the output tiles);
@@ -144,7 +145,7 @@ typedef enum hk_layout {
  *
  * clock_stamps: NULL, or a caller-owned device buffer of 32 uint64_t (256
  * bytes, 16-byte aligned; misaligned is HK_ERROR_INVALID_VALUE) that records
- * the clocks of the launch.  The 4-wave kernels (INTERLEAVE4) write, for each
+ * the clocks of the launch.  The persistent kernels (INTERLEAVE4, PINGPONG8) write, for each
  * of the first 8 workgroups x (the first workgroup dealt to chiplet x; the
  * hardware deals workgroups to the 8 chiplets round-robin), the chiplet's
  * shader-clock counter and the constant-rate counter as the workgroup starts

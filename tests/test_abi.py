@@ -310,9 +310,12 @@ def test_plan_fp8():
     assert p["kernel_name"] == "hk_gemm_il4_fp8" and p["tile_k"] == 128
     assert p["workgroups"] == 256  # persistent: one workgroup per compute unit
     assert p["threads"] == 256 and p["lds_bytes"] == 131072
-    # the ping-pong kernel on request: one workgroup per tile
+    # the ping-pong kernel on request: persistent as well
     p = _plan(hk.HK_DTYPE_FP8_E4M3, 8192, 8192, 8192, schedule="pingpong8")
-    assert p["kernel_name"] == "hk_gemm_pp8_fp8" and p["workgroups"] == 1024
+    assert p["kernel_name"] == "hk_gemm_pp8_fp8" and p["workgroups"] == 256
+    assert p["threads"] == 512
+    p = _plan(hk.HK_DTYPE_FP8_E4M3, 512, 768, 1024, schedule="pingpong8")
+    assert p["workgroups"] == 6  # fewer tiles than compute units: one workgroup each
 
 
 @pytest.mark.parametrize("K,lda,Aoff", [(60, 60, 0), (64, 66, 0), (64, 64, 2)])

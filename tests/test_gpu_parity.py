@@ -458,15 +458,16 @@ def test_k_tail_probe_ragged():
 
 # ---------------------------------------------------------------- clock record
 #
-# hk_gemm_opts.clock_stamps: the 4-wave kernels write, for workgroups 0-7, the
+# hk_gemm_opts.clock_stamps: the persistent kernels write, for workgroups 0-7, the
 # shader-clock and constant-rate counters at their start and end.  The record
 # must leave the product untouched and write nothing outside its 32 words.
 
 STAMP_SENTINEL = 0x5A5A5A5A5A5A5A5A
 
 
+@pytest.mark.parametrize("schedule", ["interleave4", "pingpong8"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_clock_record_leaves_results_unchanged(dtype):
+def test_clock_record_leaves_results_unchanged(dtype, schedule):
     M, N, K = 1024, 2048, 512  # 32 tiles: every chiplet gets a first workgroup
     if dtype == "bf16":
         A_cpu, B_cpu = _bf16(M, K, "int4", 71), _bf16(N, K, "int4", 72)
@@ -477,13 +478,13 @@ def test_clock_record_leaves_results_unchanged(dtype):
         dt, sa, sb = hk.HK_DTYPE_FP8_E4M3, 0.5, 4.0
     A, B = A_cpu.cuda(), B_cpu.cuda()
     stamps = torch.full((40,), STAMP_SENTINEL, dtype=torch.int64, device="cuda")
-    plain = _run(dt, A, B, M, N, K, K, K, N, sa, sb, schedule="interleave4")
-    rec = _run(dt, A, B, M, N, K, K, K, N, sa, sb, schedule="interleave4", clock_stamps=stamps)
+    plain = _run(dt, A, B, M, N, K, K, K, N, sa, sb, schedule=schedule)
+    rec = _run(dt, A, B, M, N, K, K, K, N, sa, sb, schedule=schedule, clock_stamps=stamps)
     assert torch.equal(_as_i16(plain), _as_i16(rec))
     st = stamps.cpu().tolist()
     assert st[32:] == [STAMP_SENTINEL] * 8
     ghz = hk.chiplet_clocks_ghz(st[:32], hk.hk_wall_clock_khz())
-    _say("clock record", dtype, [None if g is None else round(g, 3) for g in ghz])
+    _say("clock record", dtype, schedule, [None if g is None else round(g, 3) for g in ghz])
     for x in range(8):
         t0, r0, t1, r1 = st[4 * x:4 * x + 4]
         assert STAMP_SENTINEL not in (t0, r0, t1, r1) and t1 > t0 and r1 > r0, (x, st)
