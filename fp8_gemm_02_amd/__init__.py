@@ -37,6 +37,10 @@ HK_GRID_AUTO = 0
 HK_GRID_ROW_MAJOR = 1
 HK_GRID_XCD = 2
 
+HK_REPACK_AUTO = 0
+HK_REPACK_NEVER = 1
+HK_REPACK_ALWAYS = 2
+
 HK_LAYOUT_K_CONTIGUOUS = 0  # A stored M x K, B stored N x K
 HK_LAYOUT_K_STRIDED = 1     # A stored K x M, B stored K x N
 
@@ -44,10 +48,11 @@ SCHEDULES = {"auto": 0, "pingpong8": 1, "interleave4": 2, "basic": 3, "interleav
              "smalltile": 5, "producer_consumer": 6}
 GRID_ORDERS = {"auto": 0, "row_major": 1, "xcd": 2}
 LAYOUTS = {"k_contiguous": 0, "k_strided": 1}
+REPACKS = {"auto": 0, "never": 1, "always": 2}
 
 EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-            "hk_grid_map", "hk_status_string", "hk_version", "hk_wall_clock_khz",
-            "hk_attn_fwd_bf16")
+            "hk_gemm_workspace_size", "hk_grid_map", "hk_status_string", "hk_version",
+            "hk_wall_clock_khz", "hk_attn_fwd_bf16")
 
 
 class HKError(RuntimeError):
@@ -60,7 +65,9 @@ class GemmOpts(ctypes.Structure):
     _fields_ = [("schedule", ctypes.c_int32), ("grid_order", ctypes.c_int32),
                 ("group_m", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
-                ("clock_stamps", ctypes.c_void_p)]
+                ("clock_stamps", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_int64), ("repack", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class AttnStrides(ctypes.Structure):
@@ -104,6 +111,8 @@ def lib():
                              ctypes.POINTER(GemmOpts), vp]
     L.hk_gemm_plan.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                ctypes.POINTER(GemmOpts), ctypes.POINTER(PlanInfo)]
+    L.hk_gemm_workspace_size.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                         ctypes.POINTER(GemmOpts), ctypes.POINTER(i64)]
     L.hk_grid_map.argtypes = [i32, i64, i64, i32, i32, i32, i64, vp, vp, vp]
     L.hk_status_string.argtypes = [i32]
     L.hk_status_string.restype = ctypes.c_char_p
@@ -112,7 +121,8 @@ def lib():
     L.hk_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32,
                                    ctypes.POINTER(AttnStrides), vp]
     for name in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-                 "hk_grid_map", "hk_version", "hk_wall_clock_khz", "hk_attn_fwd_bf16"):
+                 "hk_gemm_workspace_size", "hk_grid_map", "hk_version", "hk_wall_clock_khz",
+                 "hk_attn_fwd_bf16"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -140,7 +150,7 @@ def _stream(s) -> int:
 
 
 def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
-          clock_stamps=None):
+          clock_stamps=None, workspace=None, workspace_bytes=None, repack=0):
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
     if isinstance(grid_order, str):
@@ -151,6 +161,12 @@ def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
     o.schedule, o.grid_order, o.group_m, o.window = schedule, grid_order, group_m, window
     o.layout_a, o.layout_b = layout_a, layout_b
     o.clock_stamps = _ptr(clock_stamps) or None
+    o.workspace = _ptr(workspace) or None
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    o.workspace_bytes = int(workspace_bytes)
+    o.repack = REPACKS[repack] if isinstance(repack, str) else int(repack)
     return o
 
 
@@ -182,10 +198,15 @@ def hk_gemm_mxfp8(A, B, C, M, N, K, lda, ldb, ldc, scales_a, scales_b, ld_scales
 
 def hk_gemm_ex(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,
                schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
-               stream=None, raise_on_error=True, clock_stamps=None):
+               stream=None, raise_on_error=True, clock_stamps=None, workspace=None,
+               workspace_bytes=None, repack=0):
     """clock_stamps: None, or a 16-byte aligned device buffer of 32 uint64 (a
-    torch tensor or a pointer) for the launch's clock record."""
-    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b, clock_stamps)
+    torch tensor or a pointer) for the launch's clock record.  workspace: None,
+    or a 256-byte aligned device buffer (tensor: its size is taken; pointer:
+    give workspace_bytes) for repacked operands; repack: "auto", "never",
+    "always" (or the HK_REPACK_* value)."""
+    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b, clock_stamps,
+              workspace, workspace_bytes, repack)
     st = lib().hk_gemm_ex(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                           float(scale_a), float(scale_b), ctypes.byref(o), _stream(stream))
     return _check(st, "hk_gemm_ex", raise_on_error)
@@ -200,6 +221,17 @@ def hk_gemm_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, schedule=0, grid_order=
                             ctypes.byref(o), ctypes.byref(info))
     _check(st, "hk_gemm_plan", True)
     return info.as_dict()
+
+
+def hk_gemm_workspace_size(dtype, A, B, C, M, N, K, lda, ldb, ldc, schedule=0, grid_order=0,
+                           group_m=0, window=0, layout_a=0, layout_b=0, repack=0):
+    """Workspace bytes hk_gemm_ex would use for repacked operands (0 = none)."""
+    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b, repack=repack)
+    out = ctypes.c_int64(0)
+    st = lib().hk_gemm_workspace_size(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb,
+                                      ldc, ctypes.byref(o), ctypes.byref(out))
+    _check(st, "hk_gemm_workspace_size", True)
+    return int(out.value)
 
 
 def hk_grid_map(grid_order, tiles_m, tiles_n, group_m, window, nxcd, wg):

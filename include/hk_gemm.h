@@ -141,6 +141,34 @@ typedef enum hk_layout {
 } hk_layout;
 
 /*
+ * Repacking an operand whose rows straddle cache lines.  The fast schedules
+ * fetch each operand row in 128-byte segments of K.  When a K-contiguous
+ * operand's row stride in bytes is not a multiple of 128 (lda = 8200 BF16
+ * elements is 16 400 bytes), every segment but one in eight spans two cache
+ * lines, which doubles the lines the loads touch: measured on MI355X, the
+ * BF16 8191 x 28670 x 8200 product ran 3212 us as given against 2611-2707 us
+ * on the same values copied to a padded stride.  With a workspace, the call
+ * first copies such an operand (all M or N rows, K elements each) to a
+ * stride that is a whole number of cache lines (the row bytes rounded up to
+ * a multiple of 1024, plus 1024 when that is a multiple of 8192), then runs
+ * the product on the copy.  The result is bit-identical either way.
+ *   REPACK_AUTO    repack when the product is large enough to pay for the
+ *                  copy (M*N >= 4096*(M+N)) and the workspace suffices;
+ *                  otherwise run on the operands as given;
+ *   REPACK_NEVER   never;
+ *   REPACK_ALWAYS  repack every straddling K-contiguous operand, whatever
+ *                  the size (HK_ERROR_INVALID_VALUE if the workspace is too
+ *                  small).
+ * Repacking applies to the fast schedules only (not BASIC) and to
+ * K-contiguous operands only; hk_gemm_workspace_size reports the bytes.
+ */
+typedef enum hk_repack {
+    HK_REPACK_AUTO = 0,
+    HK_REPACK_NEVER = 1,
+    HK_REPACK_ALWAYS = 2
+} hk_repack;
+
+/*
  * Optional knobs for hk_gemm_ex.  Zero-initialise for the defaults.
  *
  * clock_stamps: NULL, or a caller-owned device buffer of 32 uint64_t (256
@@ -155,6 +183,13 @@ typedef enum hk_layout {
  * workgroups that do not exist, and the whole buffer under any other
  * schedule, are left untouched.  The kernels and their results are the same
  * with or without it.
+ *
+ * workspace, workspace_bytes: NULL and 0, or a caller-owned device buffer
+ * (256-byte aligned; otherwise HK_ERROR_INVALID_VALUE) the call may use for
+ * repacked operands (hk_repack above).  Its contents on entry do not matter
+ * and are not preserved; it must stay valid until the call's work has
+ * completed on the stream, and two calls that may run at the same time need
+ * two workspaces.
  */
 typedef struct hk_gemm_opts {
     int32_t schedule;    /* hk_schedule */
@@ -164,6 +199,10 @@ typedef struct hk_gemm_opts {
     int32_t layout_a;    /* hk_layout of A */
     int32_t layout_b;    /* hk_layout of B */
     uint64_t *clock_stamps; /* NULL, or 32 words of clock record (above) */
+    void *workspace;        /* NULL, or device memory for repacked operands */
+    int64_t workspace_bytes; /* its size in bytes */
+    int32_t repack;      /* hk_repack */
+    int32_t reserved;    /* must be zero */
 } hk_gemm_opts;
 
 /* What a call with these arguments would launch (filled by hk_gemm_plan). */
@@ -235,6 +274,15 @@ hk_status hk_gemm_plan(int32_t dtype, const void *A, const void *B, const void *
                        int64_t M, int64_t N, int64_t K,
                        int64_t lda, int64_t ldb, int64_t ldc,
                        const hk_gemm_opts *opts, hk_gemm_plan_info *out);
+
+/* Workspace bytes a hk_gemm_ex call with these arguments would use for
+ * repacked operands (0 if it would repack nothing), assuming a workspace at
+ * least that large; opts->workspace and workspace_bytes are ignored here.
+ * Same validation as hk_gemm_plan; pointers only matter for alignment. */
+hk_status hk_gemm_workspace_size(int32_t dtype, const void *A, const void *B, const void *C,
+                                 int64_t M, int64_t N, int64_t K,
+                                 int64_t lda, int64_t ldb, int64_t ldc,
+                                 const hk_gemm_opts *opts, int64_t *bytes);
 
 /* Host evaluation of the workgroup-to-tile map used on the device (the
  * same code), for tests and locality models.  For each p < count, maps

@@ -108,11 +108,13 @@ def test_ex_rejects_bad_dtype_and_options(L):
 def test_opts_struct_matches_the_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct hk_gemm_opts \{(.*?)\} hk_gemm_opts;", text, re.S).group(1)
-    fields = re.findall(r"(int32_t|uint64_t \*)\s*(\w+);", body)
-    ctype = {"int32_t": ctypes.c_int32, "uint64_t *": ctypes.c_void_p}
+    fields = re.findall(r"(int32_t|int64_t|uint64_t \*|void \*)\s*(\w+);", body)
+    ctype = {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "uint64_t *": ctypes.c_void_p,
+             "void *": ctypes.c_void_p}
     assert [(n, ctype[t]) for t, n in fields] == list(hk.GemmOpts._fields_)
-    assert ctypes.sizeof(hk.GemmOpts) == 32
-    assert hk.GemmOpts.clock_stamps.offset == 24
+    assert ctypes.sizeof(hk.GemmOpts) == 56
+    assert hk.GemmOpts.clock_stamps.offset == 24 and hk.GemmOpts.workspace.offset == 32
+    assert hk.GemmOpts.workspace_bytes.offset == 40 and hk.GemmOpts.repack.offset == 48
 
 
 def test_chiplet_clocks_from_a_record():
@@ -441,3 +443,51 @@ def test_plan_fp8_strided_layouts():
                  ldb=1024)["kernel_name"] == "hk_gemm_il4_fp8_bkn"
     with pytest.raises(hk.HKError):
         _plan(hk.HK_DTYPE_MXFP8_E4M3, 1024, 1024, 1024, layout_b=1, ldb=1024)
+
+
+# Repacking straddling operands into a caller-provided workspace.
+def test_repack_options_are_validated(L):
+    def ex(**f):
+        o = hk.GemmOpts()
+        for k, v in f.items():
+            setattr(o, k, v)
+        return L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
+                            ctypes.byref(o), None)
+    assert ex(repack=3) == hk.HK_ERROR_INVALID_VALUE
+    assert ex(repack=-1) == hk.HK_ERROR_INVALID_VALUE
+    assert ex(reserved=1) == hk.HK_ERROR_INVALID_VALUE
+    assert ex(workspace=FAKE, workspace_bytes=-1) == hk.HK_ERROR_INVALID_VALUE
+    assert ex(workspace_bytes=4096) == hk.HK_ERROR_INVALID_VALUE      # no buffer
+    assert ex(workspace=FAKE + 64, workspace_bytes=4096) == hk.HK_ERROR_INVALID_VALUE
+    # always repacking with no room for the copy (lda = 72 straddles lines)
+    o = hk._opts(repack="always")
+    st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 72, 64, 32, 1.0, 1.0, ctypes.byref(o), None)
+    assert st == hk.HK_ERROR_INVALID_VALUE
+
+
+def _ws(M, N, K, lda, ldb, dtype=0, **opts):
+    return hk.hk_gemm_workspace_size(dtype, FAKE, FAKE, FAKE, M, N, K, lda, ldb, N, **opts)
+
+
+def test_workspace_size_policy():
+    def c256(x):
+        return (x + 255) // 256 * 256
+    # the ragged MLP shape: both operands straddle (16 400-byte rows); each is
+    # copied to 17 KiB rows
+    assert _ws(8191, 28670, 8200, 8200, 8200) == c256(8191 * 17408) + c256(28670 * 17408)
+    # only the straddling operand is copied
+    assert _ws(8191, 28670, 8200, 8256, 8200) == c256(28670 * 17408)
+    # whole-line strides: nothing to do; K-strided operands are never copied
+    assert _ws(8192, 8192, 8192, 8192, 8192) == 0
+    assert _ws(8192, 8192, 8200, 8192, 8200, layout_a=1, layout_b=1) == 0
+    # too small to pay for the copy unless asked; never means never
+    assert _ws(1024, 1024, 1032, 1032, 1032) == 0
+    assert _ws(1024, 1024, 1032, 1032, 1032, repack="always") == 2 * c256(1024 * 3072)
+    assert _ws(8191, 28670, 8200, 8200, 8200, repack="never") == 0
+    # 16 KiB rows after rounding would be a multiple of 8 KiB: one KiB more
+    assert _ws(8000, 9000, 8184, 8184, 8184) == c256(8000 * 17408) + c256(9000 * 17408)
+    # FP8: 8208-byte rows (K a whole number of 16-byte chunks) round to 9 KiB
+    assert _ws(8191, 28670, 8208, 8208, 8208, dtype=1) == c256(8191 * 9216) + c256(28670 * 9216)
+    # the plain fallback (misaligned pointer) takes operands as they are
+    assert hk.hk_gemm_workspace_size(0, FAKE + 2, FAKE, FAKE, 8191, 28670, 8200, 8200, 8200,
+                                     28670) == 0
