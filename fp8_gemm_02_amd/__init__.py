@@ -51,8 +51,8 @@ LAYOUTS = {"k_contiguous": 0, "k_strided": 1}
 REPACKS = {"auto": 0, "never": 1, "always": 2}
 
 EXPORTED = ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-            "hk_gemm_workspace_size", "hk_grid_map", "hk_status_string", "hk_version",
-            "hk_wall_clock_khz", "hk_attn_fwd_bf16")
+            "hk_gemm_ex_noalloc", "hk_gemm_workspace_size", "hk_grid_map", "hk_status_string",
+            "hk_version", "hk_wall_clock_khz", "hk_attn_fwd_bf16")
 
 
 class HKError(RuntimeError):
@@ -109,6 +109,8 @@ def lib():
     L.hk_gemm_mxfp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, i64, i64, vp]
     L.hk_gemm_ex.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
                              ctypes.POINTER(GemmOpts), vp]
+    L.hk_gemm_ex_noalloc.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32,
+                                     ctypes.POINTER(GemmOpts), vp]
     L.hk_gemm_plan.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                ctypes.POINTER(GemmOpts), ctypes.POINTER(PlanInfo)]
     L.hk_gemm_workspace_size.argtypes = [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64,
@@ -121,7 +123,7 @@ def lib():
     L.hk_attn_fwd_bf16.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32,
                                    ctypes.POINTER(AttnStrides), vp]
     for name in ("hk_gemm_bf16", "hk_gemm_fp8", "hk_gemm_mxfp8", "hk_gemm_ex", "hk_gemm_plan",
-                 "hk_gemm_workspace_size", "hk_grid_map", "hk_version", "hk_wall_clock_khz",
+                 "hk_gemm_ex_noalloc", "hk_gemm_workspace_size", "hk_grid_map", "hk_version", "hk_wall_clock_khz",
                  "hk_attn_fwd_bf16"):
         getattr(L, name).restype = i32
     _lib = L
@@ -221,6 +223,22 @@ def hk_gemm_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, schedule=0, grid_order=
                             ctypes.byref(o), ctypes.byref(info))
     _check(st, "hk_gemm_plan", True)
     return info.as_dict()
+
+
+HK_NOALLOC_SCRATCH_BYTES = 256 << 20
+
+
+def hk_gemm_ex_noalloc(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,
+                       schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
+                       stream=None, raise_on_error=True, clock_stamps=None, repack=0):
+    """hk_gemm_ex with any repack workspace taken from the library's own device
+    array (HK_NOALLOC_SCRATCH_BYTES per GPU): the call allocates nothing."""
+    o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b, clock_stamps,
+              repack=repack)
+    st = lib().hk_gemm_ex_noalloc(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                  float(scale_a), float(scale_b), ctypes.byref(o),
+                                  _stream(stream))
+    return _check(st, "hk_gemm_ex_noalloc", raise_on_error)
 
 
 def hk_gemm_workspace_size(dtype, A, B, C, M, N, K, lda, ldb, ldc, schedule=0, grid_order=0,

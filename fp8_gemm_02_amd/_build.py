@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhkgemm.so")
-SOURCES = [os.path.join(CSRC, "hk_gemm.hip"), os.path.join(CSRC, "hk_attn.hip")]
+SOURCES = [os.path.join(CSRC, "hk_gemm.hip"), os.path.join(CSRC, "hk_attn.hip"),
+           os.path.join(CSRC, "hk_noalloc.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("hk_device.hpp", "hk_grid.hpp", "hk_kernels.hpp")] + [
     os.path.join(INCLUDE, "hk_gemm.h")]
 

@@ -266,6 +266,30 @@ hk_status hk_gemm_ex(int32_t dtype,
                      float scale_a, float scale_b,
                      const hk_gemm_opts *opts, hk_stream_t stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product as hk_gemm_ex, with the repack workspace (hk_repack) taken from a
+ * device array the library owns, HK_NOALLOC_SCRATCH_BYTES per GPU, held
+ * from the first such call on a GPU until the process ends.  The call
+ * allocates nothing and never synchronises.  opts->workspace must be NULL and
+ * workspace_bytes 0 (HK_ERROR_INVALID_VALUE otherwise).  A call that would
+ * use more than HK_NOALLOC_SCRATCH_BYTES (hk_gemm_workspace_size; the BF16
+ * 8191 x 28670 x 8200 product needs 642 MB) returns HK_ERROR_NOT_SUPPORTED
+ * and enqueues nothing; repack = HK_REPACK_NEVER runs it on the operands as
+ * given.  Every call on one GPU shares that GPU's array: calls ordered on
+ * one stream are safe, calls that may overlap on one GPU (other streams,
+ * other host threads) race.  HK_ERROR_LAUNCH if the runtime cannot give the
+ * array's device address.
+ */
+#define HK_NOALLOC_SCRATCH_BYTES ((int64_t)256 << 20)
+hk_status hk_gemm_ex_noalloc(int32_t dtype,
+                             const void *A, const void *B, void *C,
+                             int64_t M, int64_t N, int64_t K,
+                             int64_t lda, int64_t ldb, int64_t ldc,
+                             float scale_a, float scale_b,
+                             const hk_gemm_opts *opts, hk_stream_t stream);
+
 /* Describe the launch hk_gemm_ex would make, without touching the GPU
  * beyond reading (once) the current device's CU count.  Pointers only
  * matter for their alignment and may be any value.  Returns the same
