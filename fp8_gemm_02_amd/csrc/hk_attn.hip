@@ -5,18 +5,27 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
 
 #include "hk_attn.h"
 #include "hk_attn.hpp"
 
-// Two buffers of a K and a V block image: 4 x 64 x D bf16.
+// Two buffers of a K and a V block image: 4 x 64 x D bf16.  Without a mask
+// one workgroup per 128-query block (the hardware's dispatch keeps the
+// compute units fed); with a causal mask a persistent grid over pairs of
+// query blocks, the longest with the shortest, so that every workgroup does
+// the same work (measured at B=4, H=16, N=4096, D=128: 988 against 889
+// TFLOP/s; without the mask the persistent form lost, 1067 against 1106).
 #define HK_ATTN_KERNEL(NAME, D, CAUSAL)                                           \
-    extern "C" __global__ void __launch_bounds__(hk::kAttnThreads, 2)             \
-        NAME(hk::AttnArgs g) {                                                    \
+    extern "C" __global__ void __launch_bounds__(                                 \
+        hk::kAttnThreads, (CAUSAL) ? hk::attn_slots<(D)>() : 2) NAME(hk::AttnArgs g) { \
         __shared__ hk::i32x4 lds[4 * hk::kAttnKV * (D) * 2 / 16];                 \
-        hk::attn_fwd_body<(D), (CAUSAL)>(g, (HK_LDS uint8_t*)lds);                \
+        if constexpr (CAUSAL)                                                     \
+            hk::attn_fwd_persist<(D), true>(g, (HK_LDS uint8_t*)lds);             \
+        else                                                                      \
+            hk::attn_fwd_body<(D), false>(g, (HK_LDS uint8_t*)lds);               \
     }
 
 HK_ATTN_KERNEL(hk_attn_fwd_d64, 64, false)
@@ -29,6 +38,30 @@ namespace {
 constexpr int64_t kMaxBytes = (int64_t)1 << 31;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int32_t g_cu_count[kMaxDevices];
+
+// Compute units of the current device (read once per device); 256 (MI355X)
+// when the runtime cannot say.
+int32_t cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::call_once(g_cu_once[dev], [dev]() {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0) {
+            (void)hipGetLastError();
+            cus = 256;
+        }
+        g_cu_count[dev] = cus;
+    });
+    return g_cu_count[dev];
+}
 
 }  // namespace
 
@@ -84,8 +117,16 @@ extern "C" hk_status hk_attn_fwd_bf16(const void* Q, const void* K, const void* 
     memcpy(g.sk, st.k, sizeof g.sk);
     memcpy(g.sv, st.v, sizeof g.sv);
     memcpy(g.so, st.o, sizeof g.so);
-    const int64_t grid = B * Hq * g.nqb;
-    if (grid > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
+    // work units: query blocks, or under a causal mask pairs of them (the
+    // longest with the shortest)
+    g.upH = causal ? (g.nqb + 1) / 2 : g.nqb;
+    if (B * Hq * g.nqb > INT32_MAX) return HK_ERROR_NOT_SUPPORTED;
+    g.nunits = (int32_t)(B * Hq * g.upH);
+    // causal: persistent, as many workgroups per compute unit as its
+    // registers take; otherwise one workgroup per query block
+    const int64_t slots = (D == 64 ? hk::attn_slots<64>() : hk::attn_slots<128>()) *
+                          (int64_t)cu_count();
+    const int64_t grid = !causal ? B * Hq * g.nqb : g.nunits < slots ? g.nunits : slots;
 
     const void* kern = D == 64 ? (causal ? (const void*)hk_attn_fwd_d64_causal
                                          : (const void*)hk_attn_fwd_d64)

@@ -219,3 +219,21 @@ def test_attn_full_size_sampled(name):
          "lse err/bound %.3g" % (np.abs(lse - ref_lse) / lbound).max())
     assert st["ok"], st
     assert (np.abs(lse - ref_lse) <= lbound).all()
+
+
+# The causal kernels are persistent: a grid of as many workgroups as the
+# compute units hold (2 per unit at D = 128, 3 at D = 64) walks pairs of query
+# blocks (the longest with the shortest; the middle block alone when their
+# count is odd), prefetching each next tile's first key block during the
+# current tile's last.  Shapes with more pairs than workgroups make some
+# workgroups run several tiles in a row, with ragged N, an odd number of query
+# blocks and grouped-query heads; compared in full.
+@pytest.mark.parametrize("B,Hq,Hkv,N,D", [(4, 48, 16, 600, 128), (3, 96, 32, 600, 64),
+                                          (2, 40, 40, 1300, 128)])
+def test_attn_causal_persistent_several_tiles_per_workgroup(B, Hq, Hkv, N, D):
+    nqb = (N + 127) // 128
+    units = B * Hq * ((nqb + 1) // 2)
+    slots = (3 if D == 64 else 2) * 256
+    assert units > slots or B * Hq * nqb > slots  # several tiles in a row somewhere
+    q, k, v = _qkv(B, Hq, Hkv, N, D, 300 + D)
+    _check(q, k, v, True, tag="persistent causal, %d pairs" % units)
