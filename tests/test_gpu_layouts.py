@@ -112,8 +112,11 @@ def test_bf16_both_strided_any_k(K):
 
 
 @pytest.mark.parametrize("layouts", LAYOUTS)
-def test_bf16_layouts_padded_strides_poisoned(layouts):
-    M, N, K = 520, 264, 392
+@pytest.mark.parametrize("K", [392, 1000])
+def test_bf16_layouts_padded_strides_poisoned(layouts, K):
+    # K = 1000: 15 whole stages, so the loop that loads interior tiles'
+    # whole stages without a range check runs many times over padded rows
+    M, N = 520, 264
     la, lb = layouts
     lda = (M if la else K) + 24
     ldb = (N if lb else K) + 40
@@ -190,8 +193,12 @@ def test_fp8_both_strided_any_k(K):
 
 
 @pytest.mark.parametrize("layouts", LAYOUTS)
-def test_fp8_layouts_padded_strides_poisoned(layouts):
-    M, N, K = 528, 272, 400
+@pytest.mark.parametrize("K", [400, 1040])
+def test_fp8_layouts_padded_strides_poisoned(layouts, K):
+    # K = 400 is only 3 whole 128-byte stages, which never reach the loop that
+    # loads interior tiles' whole stages without a range check; K = 1040 (8
+    # whole stages and a tail) runs it three times over padded rows
+    M, N = 528, 272
     la, lb = layouts
     lda = (M if la else K) + 32
     ldb = (N if lb else K) + 48
