@@ -23,6 +23,7 @@ import torch
 import fp8_gemm_02_amd as hk
 import gemm_inputs
 import oracle
+from oracle import matmul as oracle_matmul
 
 pytestmark = pytest.mark.gpu
 
@@ -275,9 +276,10 @@ def test_matmul_fp8_views():
         assert st["ok"], (name, st)
 
 
-def test_bf16_8192_b_stored_kn_sampled():
+def test_bf16_8192_b_stored_kn_full_size():
     """The B-stored-K-x-N workload exactly as the benchmark launches it,
-    checked on sampled entries (random plus the corners of edge tiles)."""
+    checked on sampled entries (random plus the corners of edge tiles) with the
+    oracle's loop and on every element with its matmul path."""
     w = gemm_inputs.WORKLOADS["bf16_8192_bkn"]
     x = gemm_inputs.make_inputs(w)
     A_st, B_st = gemm_inputs.stored(w, x)
@@ -301,11 +303,17 @@ def test_bf16_8192_b_stored_kn_sampled():
     st = oracle.compare(got[rows, cols], ref, S, rel_tol=RTOL)
     _say("bf16_8192_bkn sampled", rows.size, {k: st[k] for k in st if k != "ulp_hist"})
     assert st["ok"], st
+    ref, S = oracle_matmul.gemm_by_matmul("bf16", gemm_inputs.bits(x["A"]), gemm_inputs.bits(x["B"]),
+                                          w.M, w.N, w.K)
+    st = oracle.compare(got, ref, S, rel_tol=RTOL)
+    _say("bf16_8192_bkn every element", {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
 
 
-def test_fp8_8192_b_stored_kn_sampled():
+def test_fp8_8192_b_stored_kn_full_size():
     """The FP8 B-stored-K-x-N workload as the benchmark launches it (4-wave
-    kernel, transposing 8-bit reads), on sampled entries."""
+    kernel, transposing 8-bit reads), on sampled entries with the oracle's loop
+    and on every element with its matmul path."""
     w = gemm_inputs.WORKLOADS["fp8_8192_bkn"]
     x = gemm_inputs.make_inputs(w)
     A_st, B_st = gemm_inputs.stored(w, x)
@@ -329,4 +337,9 @@ def test_fp8_8192_b_stored_kn_sampled():
                                  scale_a=x["scale_a"], scale_b=x["scale_b"])
     st = oracle.compare(got[rows, cols], ref, S, rel_tol=RTOL)
     _say("fp8_8192_bkn sampled", rows.size, {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
+    ref, S = oracle_matmul.gemm_by_matmul("fp8", gemm_inputs.bits(x["A"]), gemm_inputs.bits(x["B"]),
+                                          w.M, w.N, w.K, scale_a=x["scale_a"], scale_b=x["scale_b"])
+    st = oracle.compare(got, ref, S, rel_tol=RTOL)
+    _say("fp8_8192_bkn every element", {k: st[k] for k in st if k != "ulp_hist"})
     assert st["ok"], st

@@ -16,6 +16,7 @@ import torch
 import fp8_gemm_02_amd as hk
 import gemm_inputs
 import oracle
+from oracle import matmul as oracle_matmul
 
 pytestmark = pytest.mark.gpu
 
@@ -113,9 +114,10 @@ def test_mxfp8_persistent_tile_walk():
     _check(A, B, SA, SB, M, N, K, exact=True)
 
 
-def test_mxfp8_full_size_sampled():
+def test_mxfp8_full_size():
     """The 8192^3 workload exactly as the benchmark launches it (packed
-    scales, ld = K / 32 = 256), checked on sampled entries."""
+    scales, ld = K / 32 = 256), checked on sampled entries with the oracle's
+    loop and on every element with its matmul path."""
     w = gemm_inputs.WORKLOADS["mxfp8_8192"]
     x = gemm_inputs.make_inputs(w)
     nb = w.K // 32
@@ -128,6 +130,11 @@ def test_mxfp8_full_size_sampled():
                                   rows, cols)
     st = oracle.compare(got[rows, cols], c, s, rel_tol=RTOL)
     _say("mxfp8_8192 sampled", {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
+    ref, S = oracle_matmul.gemm_mx_by_matmul(gemm_inputs.bits(x["A"]), gemm_inputs.bits(x["B"]),
+                                             x["SA"].numpy(), x["SB"].numpy(), w.M, w.N, w.K)
+    st = oracle.compare(got, ref, S, rel_tol=RTOL)
+    _say("mxfp8_8192 every element", {k: st[k] for k in st if k != "ulp_hist"})
     assert st["ok"], st
 
 

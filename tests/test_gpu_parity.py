@@ -22,6 +22,7 @@ import torch
 import fp8_gemm_02_amd as hk
 import gemm_inputs
 import oracle
+from oracle import matmul as oracle_matmul
 
 pytestmark = pytest.mark.gpu
 
@@ -600,6 +601,23 @@ def test_full_size_integer_exact_everywhere(name, schedule):
     assert bad == 0
 
 
+@pytest.mark.parametrize("name,schedule", [("bf16_8192", None), ("bf16_8192", "pingpong8"),
+                                           ("bf16_mlp", None), ("fp8_8192", None)])
+def test_full_size_random_compared_in_full(name, schedule):
+    """Random inputs at full size, every output element against the oracle
+    (its matmul path, pinned to the loop on the CPU)."""
+    w = gemm_inputs.WORKLOADS[name]
+    x = gemm_inputs.make_inputs(w)
+    C = _launch_default(w, x, **({"schedule": schedule} if schedule else {}))
+    got = _bits16(C)
+    del C
+    ref, S = oracle_matmul.gemm_by_matmul(w.dtype, gemm_inputs.bits(x["A"]), gemm_inputs.bits(x["B"]),
+                                          w.M, w.N, w.K, scale_a=x["scale_a"], scale_b=x["scale_b"])
+    st = oracle.compare(got, ref, S, rel_tol=RTOL)
+    _say(name, schedule or "default", "every element", {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
+
+
 def test_pingpong8_8192_sampled():
     w = gemm_inputs.WORKLOADS["bf16_8192"]
     x = gemm_inputs.make_inputs(w)
@@ -659,8 +677,9 @@ def test_repack_always_matches_oracle_and_direct(dtype, M, N, K, pad, schedule):
 def test_ragged_full_size_with_workspace():
     """The ragged MLP shape in the launch configuration the bench times for it:
     hk_gemm_ex with a workspace, which copies both operands (16 400-byte rows)
-    to 17 KiB rows.  Bit-identical to the direct call, sampled against the
-    oracle, and integer-valued inputs exact everywhere."""
+    to 17 KiB rows.  Bit-identical to the direct call, compared with the
+    oracle on every element (and on a sample with its loop), and
+    integer-valued inputs exact everywhere."""
     w = gemm_inputs.WORKLOADS["bf16_mlp_ragged"]
     M, N, K = w.M, w.N, w.K
     fake = 1 << 20  # the query only looks at alignment
@@ -689,4 +708,10 @@ def test_ragged_full_size_with_workspace():
                                          gemm_inputs.bits(x["B"]).ravel(), M, N, K, rows, cols)
             st = oracle.compare(got, ref, S, rel_tol=RTOL)
             _say(w.name, "repacked, sampled", rows.size, {k: st[k] for k in st if k != "ulp_hist"})
+            assert st["ok"], st
+            got = _bits16(rep)
+            ref, S = oracle_matmul.gemm_by_matmul("bf16", gemm_inputs.bits(x["A"]),
+                                                  gemm_inputs.bits(x["B"]), M, N, K)
+            st = oracle.compare(got, ref, S, rel_tol=RTOL)
+            _say(w.name, "repacked, every element", {k: st[k] for k in st if k != "ulp_hist"})
             assert st["ok"], st

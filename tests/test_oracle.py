@@ -389,3 +389,58 @@ def test_compare_rule(oracle_mod):
     nan = oracle_mod.compare(np.array([0x7FC0], np.uint16), np.array([0x3F80], np.uint16),
                              np.array([1e6]))
     assert not nan["ok"]
+
+
+def _rule_one(g: int, r: int, s: float, rel_tol: float):
+    """The acceptance rule for one element, written out: (ok, ulps or -1, err/bound)."""
+    gv = float(oracle_bits_to_f64(g))
+    rv = float(oracle_bits_to_f64(r))
+    if g == r or (g & 0x7FFF) == 0 == (r & 0x7FFF):
+        return True, (0 if math.isfinite(gv) else -1), 0.0
+    err = abs(gv - rv)
+    ax = abs(rv)
+    E = max(math.frexp(ax)[1] - 1, -126) if ax > 0 and math.isfinite(ax) else -126
+    ulp = 2.0 ** (E - 7)
+    bound = ulp + rel_tol * s
+    ok = math.isfinite(gv) and err <= bound
+    ulps = round(err / ulp) if math.isfinite(err) else -1
+    ratio = err / bound if math.isfinite(err) else math.inf
+    return ok, ulps, ratio
+
+
+def oracle_bits_to_f64(b: int) -> float:
+    return float(np.array([b << 16], dtype=np.uint32).view(np.float32)[0])
+
+
+def test_compare_matches_the_rule_element_by_element(oracle_mod):
+    """The comparator against the rule evaluated one element at a time, on
+    identical, nearby, signed-zero, NaN and infinite entries."""
+    rng = np.random.default_rng(21)
+    n = 3000
+    r = _random_bf16_bits(rng, n, -20, 20)
+    g = r.copy()
+    kind = rng.integers(0, 8, n)
+    step = rng.integers(1, 4, n).astype(np.uint16)
+    g = np.where(kind == 1, r + step, g)
+    g = np.where(kind == 2, r - step, g)
+    g = np.where(kind == 3, r ^ 0x8000, g)                 # sign flipped
+    g = np.where(kind == 4, np.uint16(0x7FC0), g)          # NaN on the GPU side
+    r = np.where(kind == 5, np.uint16(0x7F80), r)          # infinity in the reference
+    g = np.where(kind == 6, np.uint16(0x8000), g)
+    r = np.where(kind == 6, np.uint16(0x0000), r)          # -0 against +0
+    g = g.astype(np.uint16)
+    r = r.astype(np.uint16)
+    S = np.where(rng.random(n) < 0.2, 0.0, np.abs(rng.standard_normal(n)) * 2.0 ** rng.integers(-20, 20, n))
+    st = oracle_mod.compare(g, r, S, rel_tol=1e-4)
+    want = [_rule_one(int(a), int(b), float(c), 1e-4) for a, b, c in zip(g, r, S)]
+    bad = [i for i, w in enumerate(want) if not w[0]]
+    assert st["violations"] == len(bad) and st["ok"] == (not bad)
+    assert st["first_bad"][0] == bad[0]
+    hist = {}
+    for _, u, _ in want:
+        u = min(max(u, -1), 8)
+        hist[u] = hist.get(u, 0) + 1
+    assert st["ulp_hist"] == dict(sorted(hist.items()))
+    assert st["max_err_over_bound"] == max(w[2] for w in want)
+    assert st["bit_identical_frac"] == sum(1 for a, b in zip(g, r)
+                                            if a == b or (a & 0x7FFF) == 0 == (b & 0x7FFF)) / n
