@@ -23,6 +23,12 @@ same bf16 value unless the exact sum lies that close to a bf16 rounding
 boundary.  This is what makes a full-size comparison cost seconds instead of
 minutes.  The loop oracle stays the reference; these functions are pinned to
 it and to the same closed forms and fixtures in the CPU tests.
+
+``attention_by_matmul`` does the same for the attention forward (the pages'
+second workload: "How to make AMD GPUs go brrr", section "Real kernel example";
+"HipKittens", section "Performance results"): textbook scaled dot-product
+attention over BF16 inputs, its scores and weighted sums over a block of query
+rows taken by library matrix products.
 """
 from __future__ import annotations
 
@@ -107,3 +113,77 @@ def gemm_mx_by_matmul(A: np.ndarray, B: np.ndarray, SA: np.ndarray, SB: np.ndarr
         if want_s:
             S[r0:r1] = np.abs(a) @ b_abs.T
     return C, S
+
+
+def _head(X: np.ndarray, s, b: int, h: int, N: int, D: int) -> np.ndarray:
+    """The N x D token rows of head (b, h), decoded exactly to double."""
+    flat = np.ascontiguousarray(X).ravel()
+    if N == 0:
+        return np.zeros((0, D), dtype=np.float64)
+    off = int(b * s[0] + h * s[1])
+    v = np.lib.stride_tricks.as_strided(flat[off:], shape=(N, D),
+                                        strides=(int(s[2]) * flat.itemsize, flat.itemsize),
+                                        writeable=False)
+    return oracle.bf16_to_f64(v)
+
+
+def attention_by_matmul(Q, K, V, B: int, Hq: int, Hkv: int, N: int, D: int, scale: float,
+                        causal: bool, q_strides=None, k_strides=None, v_strides=None, rows=None,
+                        rows_per_chunk: int = 512):
+    """The attention forward of ``oracle.attention`` (same arguments and results).
+
+    The loop oracle's steps on a block of query rows at a time: scores
+    s_j = scale * q . k_j by a library matrix product (keys past the query
+    masked out when causal), m = max_j s_j, p_j = exp(s_j - m), l = sum_j p_j,
+    O = RNE_bf16(sum_j p_j v_j / l), LSE = m + log(l) and the tolerance
+    magnitude A = sum_j p_j |v_j| / l.  Query head h reads key/value head
+    h / (Hq / Hkv).  Only the order of the double additions differs.
+    """
+    Q = oracle._as_bits(Q, oracle.BF16)
+    K = oracle._as_bits(K, oracle.BF16)
+    V = oracle._as_bits(V, oracle.BF16)
+    if B < 0 or Hq < 1 or Hkv < 1 or N < 0 or D < 1 or Hq % Hkv != 0:
+        raise ValueError("invalid attention shape")
+    sq = oracle._strides(q_strides, Hq, N, D)
+    sk = oracle._strides(k_strides, Hkv, N, D)
+    sv = oracle._strides(v_strides, Hkv, N, D)
+    for X, s, H in ((Q, sq, Hq), (K, sk, Hkv), (V, sv, Hkv)):
+        if B * H * N > 0 and X.size < (B - 1) * s[0] + (H - 1) * s[1] + (N - 1) * s[2] + D:
+            raise ValueError("operand too small for its shape and strides")
+    total = B * Hq * N
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        if rows.size and (rows.min() < 0 or rows.max() >= total):
+            raise ValueError("row index out of range")
+    o = np.zeros((total, D), dtype=np.uint16)
+    o64 = np.zeros((total, D), dtype=np.float64)
+    lse = np.zeros(total, dtype=np.float64)
+    amag = np.zeros((total, D), dtype=np.float64)
+    group = Hq // Hkv
+    keys = np.arange(N)
+    for b in range(B):
+        for kvh in range(Hkv):
+            k = _head(K, sk, b, kvh, N, D)
+            v = _head(V, sv, b, kvh, N, D)
+            v_abs = np.abs(v)
+            for h in range(kvh * group, (kvh + 1) * group):
+                q = _head(Q, sq, b, h, N, D)
+                base = (b * Hq + h) * N
+                for i0 in range(0, N, rows_per_chunk):
+                    i1 = min(i0 + rows_per_chunk, N)
+                    # with the causal mask no row of the block sees a key past i1 - 1
+                    nk = i1 if causal else N
+                    s = (q[i0:i1] @ k[:nk].T) * scale
+                    if causal:
+                        s[keys[None, :nk] > np.arange(i0, i1)[:, None]] = -np.inf
+                    m = s.max(axis=1)
+                    p = np.exp(s - m[:, None])
+                    l = p.sum(axis=1)
+                    val = (p @ v[:nk]) / l[:, None]
+                    o64[base + i0:base + i1] = val
+                    o[base + i0:base + i1] = oracle.bf16_round(val)
+                    amag[base + i0:base + i1] = (p @ v_abs[:nk]) / l[:, None]
+                    lse[base + i0:base + i1] = m + np.log(l)
+    if rows is not None:
+        return o[rows], o64[rows], lse[rows], amag[rows]
+    return o, o64, lse, amag

@@ -15,7 +15,7 @@ Shapes cover one workgroup, ragged N (a partial query block and a partial
 key block), N = 1, grouped-query heads, both head dimensions, causal and
 non-causal, strided (B, N, H, D) storage with poisoned padding, more
 workgroups than compute units, and the benchmark's workloads at full size
-(sampled rows).
+(sampled rows against the oracle's loop, every row against its matmul path).
 """
 import numpy as np
 import pytest
@@ -24,6 +24,7 @@ import torch
 import fp8_gemm_02_amd as hk
 import gemm_inputs
 import oracle
+from oracle import matmul as oracle_matmul
 
 pytestmark = pytest.mark.gpu
 
@@ -196,9 +197,10 @@ def test_attn_many_workgroups():
 
 @pytest.mark.parametrize("name", ["attn_d128_n4096", "attn_d128_n4096_causal", "attn_d64_n4096",
                                   "attn_gqa_d128_n8192_causal"])
-def test_attn_full_size_sampled(name):
-    """The benchmark's workloads as bench.py launches them, on sampled rows
-    (random plus the first and last rows of heads and query blocks)."""
+def test_attn_full_size(name):
+    """The benchmark's workloads as bench.py launches them: sampled rows
+    (random plus the first and last rows of heads and query blocks) against
+    the oracle's loop, then every row, O and LSE, against its matmul path."""
     w = gemm_inputs.ATTN_WORKLOADS[name]
     x = gemm_inputs.make_attn_inputs(w)
     rng = np.random.default_rng(7)
@@ -207,8 +209,9 @@ def test_attn_full_size_sampled(name):
     rows = np.concatenate([rng.integers(0, nrow, 400), edge])
     q, k, v = x["q"], x["k"], x["v"]
     O, L = _run(q.cuda(), k.cuda(), v.cuda(), w.causal, w.scale)
-    got = _bits(O).reshape(-1, w.D)[rows]
-    lse = L.cpu().numpy().ravel()[rows]
+    got_all = _bits(O).reshape(-1, w.D)
+    lse_all = L.cpu().numpy().ravel()
+    got, lse = got_all[rows], lse_all[rows]
     del O, L
     ref, _, ref_lse, A = oracle.attention(_bits(q).ravel(), _bits(k).ravel(), _bits(v).ravel(),
                                           w.B, w.Hq, w.Hkv, w.N, w.D, w.scale, w.causal,
@@ -219,6 +222,16 @@ def test_attn_full_size_sampled(name):
          "lse err/bound %.3g" % (np.abs(lse - ref_lse) / lbound).max())
     assert st["ok"], st
     assert (np.abs(lse - ref_lse) <= lbound).all()
+    ref, _, ref_lse, A = oracle_matmul.attention_by_matmul(_bits(q).ravel(), _bits(k).ravel(),
+                                                           _bits(v).ravel(), w.B, w.Hq, w.Hkv, w.N,
+                                                           w.D, w.scale, w.causal)
+    st = oracle.compare(got_all, ref, A, rel_tol=RTOL)
+    lbound = 1e-5 * (1 + np.abs(ref_lse)) + w.N * 2.0 ** -24
+    lratio = (np.abs(lse_all - ref_lse) / lbound).max()
+    _say(name, "every row", {k_: st[k_] for k_ in st if k_ != "ulp_hist"},
+         "lse err/bound %.3g" % lratio)
+    assert st["ok"], st
+    assert lratio <= 1.0
 
 
 # The causal kernels are persistent: a grid of as many workgroups as the

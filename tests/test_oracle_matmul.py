@@ -4,12 +4,14 @@ The matmul path computes the same product as the loop oracle with the double
 sum taken by numpy's matrix product; it is what lets the GPU tests compare
 full-size outputs element by element.  It is pinned here three ways:
 
-* every pin of test_oracle.py and test_oracle_mx.py that calls the product
-  (hand-derived fixtures, exact rationals, integer-valued products against
-  int64 and torch, identities, strides, NaN scales) runs against it, with the
-  rows taken in chunks of 5 so the chunk loop is exercised;
+* every pin of test_oracle.py, test_oracle_mx.py and test_oracle_attn.py
+  that calls the product or the attention forward (hand-derived fixtures,
+  exact rationals, integer-valued products against int64 and torch,
+  identities, strides, NaN scales; torch's float64 SDPA, mpmath, closed forms,
+  invariants) runs against it, with the rows taken in chunks of 5 so the chunk
+  loop is exercised;
 * on random operands with padded strides it agrees with the loop oracle bit
-  for bit in C and to a few double roundings in S;
+  for bit in C (and O) and to a few double roundings in S (and LSE, A);
 * planted mistakes in a copy of its source each make at least one of those
   pins fail.
 """
@@ -21,6 +23,7 @@ import pytest
 import oracle
 from oracle import matmul
 from tests import test_oracle as pins
+from tests import test_oracle_attn as attn_pins
 from tests import test_oracle_mx as mx_pins
 
 
@@ -43,6 +46,11 @@ class MatmulOracle:
                 threads=None, want_s=True):
         return self._mod.gemm_mx_by_matmul(A, B, SA, SB, M, N, K, lda, ldb, ldsa, ldsb,
                                            want_s, self._rpc)
+
+    def attention(self, Q, K, V, B, Hq, Hkv, N, D, scale, causal, q_strides=None,
+                  k_strides=None, v_strides=None, rows=None, threads=None):
+        return self._mod.attention_by_matmul(Q, K, V, B, Hq, Hkv, N, D, scale, causal, q_strides,
+                                             k_strides, v_strides, rows, self._rpc)
 
 
 PINS = {
@@ -70,6 +78,22 @@ PINS = {
     "mx_nan_scale": mx_pins.test_nan_scale_poisons_its_row_only,
     "mx_strided_equals_packed": mx_pins.test_strided_equals_packed,
     "mx_sampled_loop_equals_full": mx_pins.test_sampled_equals_full,
+    "attn_torch_sdpa": lambda m: [attn_pins.test_matches_torch_sdpa_float64(m, *p, c) for p in
+                                  [(1, 1, 1, 1, 8), (2, 4, 2, 7, 8), (1, 2, 1, 33, 64),
+                                   (1, 3, 3, 20, 16)] for c in (False, True)],
+    "attn_mpmath": lambda m: [attn_pins.test_correctly_rounded_against_mpmath(m, s, c)
+                              for s in range(3) for c in (False, True)],
+    "attn_zero_queries": lambda m: [attn_pins.test_zero_queries_give_the_mean_of_visible_values(m, c)
+                                    for c in (False, True)],
+    "attn_single_rounding": attn_pins.test_mean_that_double_rounding_gets_wrong,
+    "attn_single_key": attn_pins.test_single_key_returns_its_value_row,
+    "attn_first_causal_row": attn_pins.test_first_causal_row_sees_only_key_zero,
+    "attn_dominant_key": attn_pins.test_dominant_key_gives_its_value_row,
+    "attn_grouped_heads": attn_pins.test_grouped_query_heads_equal_repeated_heads,
+    "attn_scale_two": attn_pins.test_scale_two_equals_doubled_queries,
+    "attn_strided": attn_pins.test_strided_equals_packed,
+    "attn_rows_subset": attn_pins.test_rows_subset_equals_full,
+    "attn_rejects": attn_pins.test_rejects_bad_arguments,
 }
 
 
@@ -124,6 +148,24 @@ def test_mx_agrees_with_the_loop():
     assert np.allclose(S0, S1, rtol=K * 2.0 ** -52, atol=0)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,D,causal,chunk", [(2, 4, 2, 37, 64, True, 8),
+                                                      (1, 3, 1, 50, 128, False, 16),
+                                                      (1, 1, 1, 1, 8, True, 512),
+                                                      (2, 2, 2, 129, 32, True, 128)])
+def test_attention_agrees_with_the_loop(B, Hq, Hkv, N, D, causal, chunk):
+    q = attn_pins._bf16((B, Hq, N, D), 5 + N, 2.0)
+    k = attn_pins._bf16((B, Hkv, N, D), 6 + N, 2.0)
+    v = attn_pins._bf16((B, Hkv, N, D), 7 + N)
+    args = (attn_pins._bits(q).ravel(), attn_pins._bits(k).ravel(), attn_pins._bits(v).ravel(),
+            B, Hq, Hkv, N, D, 0.7, causal)
+    o0, v0, l0, a0 = oracle.attention(*args)
+    o1, v1, l1, a1 = matmul.attention_by_matmul(*args, rows_per_chunk=chunk)
+    assert np.array_equal(o0, o1)
+    assert np.allclose(v1, v0, rtol=1e-13, atol=1e-13 * np.abs(a0).max())
+    assert np.allclose(l1, l0, rtol=1e-14, atol=1e-14)
+    assert np.allclose(a1, a0, rtol=1e-13, atol=0)
+
+
 def test_rejects_short_operands():
     A = np.zeros(16, dtype=np.uint16)
     with pytest.raises(ValueError):
@@ -144,14 +186,36 @@ MUTANTS = {
                               "oracle.bf16_round((((a @ b.T) + 0.0) * s).astype(np.float32))"),
     "chunk_off_by_one": ("r1 = min(r0 + rows_per_chunk, M)\n        a = _decode(code",
                          "r1 = min(r0 + rows_per_chunk - 1, M)\n        a = _decode(code"),
-    "bf16_read_as_fp16": ("return oracle.bf16_to_f64(v)",
-                          "return v.view(np.float16).astype(np.float64)"),
+    "bf16_read_as_fp16": ("return oracle.bf16_to_f64(v)\n    return tab[v]",
+                          "return v.view(np.float16).astype(np.float64)\n    return tab[v]"),
+    "attn_bf16_read_as_fp16": ("writeable=False)\n    return oracle.bf16_to_f64(v)",
+                               "writeable=False)\n    return v.view(np.float16).astype(np.float64)"),
     "mx_block_of_16": ("np.repeat(x, 32, axis=1)", "np.repeat(x, 16, axis=1)"),
     "mx_scales_swapped": ("a = _decode_mx(A, SA, r0, r1, K, lda, ldsa, tab, xtab)",
                           "a = _decode_mx(A, SB, r0, r1, K, lda, ldsb, tab, xtab)"),
     "mx_scale_ignored": ("return v * np.repeat(x, 32, axis=1)[:, :K]", "return v"),
     "mx_negated": ("C[r0:r1] = oracle.bf16_round((a @ b.T) + 0.0)",
                               "C[r0:r1] = oracle.bf16_round(-(a @ b.T))"),
+    "attn_no_scale": ("s = (q[i0:i1] @ k[:nk].T) * scale", "s = q[i0:i1] @ k[:nk].T"),
+    "attn_causal_strict": ("s[keys[None, :nk] > np.arange(i0, i1)[:, None]] = -np.inf",
+                           "s[keys[None, :nk] >= np.arange(i0, i1)[:, None]] = -np.inf"),
+    "attn_causal_block_short": ("nk = i1 if causal else N", "nk = i1 - 1 if causal else N"),
+    "attn_causal_ignored": ("if causal:\n                        s[keys",
+                            "if False:\n                        s[keys"),
+    "attn_causal_chunk_relative": ("np.arange(i0, i1)[:, None]] = -np.inf",
+                                   "np.arange(0, i1 - i0)[:, None]] = -np.inf"),
+    "attn_gqa_modulo": ("for h in range(kvh * group, (kvh + 1) * group):",
+                        "for h in range(kvh, Hq, Hkv):"),
+    "attn_no_max_shift": ("p = np.exp(s - m[:, None])", "p = np.exp(s)"),
+    "attn_lse_no_log": ("lse[base + i0:base + i1] = m + np.log(l)",
+                        "lse[base + i0:base + i1] = m + l"),
+    "attn_keys_as_values": ("val = (p @ v[:nk]) / l[:, None]", "val = (p @ k[:nk]) / l[:, None]"),
+    "attn_unnormalised": ("val = (p @ v[:nk]) / l[:, None]", "val = p @ v[:nk]"),
+    "attn_amag_unnormalised": ("amag[base + i0:base + i1] = (p @ v_abs[:nk]) / l[:, None]",
+                               "amag[base + i0:base + i1] = p @ v_abs[:nk]"),
+    "attn_amag_signed": ("amag[base + i0:base + i1] = (p @ v_abs[:nk]) / l[:, None]",
+                         "amag[base + i0:base + i1] = (p @ v[:nk]) / l[:, None]"),
+    "attn_ignored_head_stride": ("off = int(b * s[0] + h * s[1])", "off = int(b * s[0] + h * N * D)"),
 }
 
 
@@ -169,7 +233,8 @@ def test_pins_catch_matmul_mutant(tmp_path, name):
     failed = []
     for pin_name, pin in PINS.items():
         try:
-            pin(proxy)
+            with np.errstate(all="ignore"):
+                pin(proxy)
         except (AssertionError, ValueError, IndexError):
             failed.append(pin_name)
     assert failed, "no pin caught mutant %s" % name
