@@ -649,15 +649,20 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         // Stage pair (t, t+1) loads stages t+2 and t+3, all inside K while
         // t + 4 <= the number of whole stages.
         uint32_t t = 0;
+        // the whole-stage count taken afresh per tile: kept across the tile
+        // loop, the compiler holds the loop-entry test in a register of its
+        // own, which spills
+        uint32_t nkw = nk_whole;
+        asm volatile("" : "+s"(nkw));
         // a tile inside C: its whole stages take the global loads
         const bool inside = cur.m0 + kIL4Tile <= g.M && cur.n0 + kIL4Tile <= g.N;
         if (inside) {
-            for (; t + 4 <= nk_whole; t += 2) {
+            for (; t + 4 <= nkw; t += 2) {
                 stage(unmasked, cur, t + 2, buf0, buf1, unchecked);
                 stage(unmasked, cur, t + 3, buf1, buf0, unchecked);
             }
         } else {
-            for (; t + 4 <= nk_whole; t += 2) {
+            for (; t + 4 <= nkw; t += 2) {
                 stage(unmasked, cur, t + 2, buf0, buf1, checked);
                 stage(unmasked, cur, t + 3, buf1, buf0, checked);
             }
@@ -1013,15 +1018,18 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         const uint32_t w_next = w + gridDim.x;
         const Tile nxt = tile(w_next);
         uint32_t t = 0;
+        // the whole-stage count taken afresh per tile (see il4_bf16_body)
+        uint32_t nkw = nk_whole;
+        asm volatile("" : "+s"(nkw));
         // a tile inside C: its whole stages take the global loads
         const bool inside = cur.m0 + kIL4Tile <= g.M && cur.n0 + kIL4Tile <= g.N;
         if (!kMx && !kAT && inside) {
-            for (; t + 4 <= nk_whole; t += 2) {
+            for (; t + 4 <= nkw; t += 2) {
                 stage(unmasked, t, cur, t + 2, seq, buf0, buf1, t + 1, seq, unchecked);
                 stage(unmasked, t + 1, cur, t + 3, seq, buf1, buf0, t + 2, seq, unchecked);
             }
         } else {
-            for (; t + 4 <= nk_whole; t += 2) {
+            for (; t + 4 <= nkw; t += 2) {
                 stage(unmasked, t, cur, t + 2, seq, buf0, buf1, t + 1, seq, checked);
                 stage(unmasked, t + 1, cur, t + 3, seq, buf1, buf0, t + 2, seq, checked);
             }
