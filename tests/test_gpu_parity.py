@@ -674,6 +674,42 @@ def test_repack_always_matches_oracle_and_direct(dtype, M, N, K, pad, schedule):
     assert st["ok"], st
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("which", ["A", "B"])
+def test_repack_one_operand(dtype, which):
+    """Only one operand's rows straddle cache lines: the copy launch takes that
+    operand's rows alone, and the workspace holds that copy alone."""
+    M, N, K = 520, 610, 272
+    esz = 2 if dtype == "bf16" else 1
+    aligned = 320 if dtype == "bf16" else 384   # rows of whole 128-byte lines
+    straddle = K + 16                           # 576 or 288 bytes: not whole lines
+    assert (aligned * esz) % 128 == 0 and (straddle * esz) % 128 != 0
+    lda, ldb = (straddle, aligned) if which == "A" else (aligned, straddle)
+    if dtype == "fp8":
+        A_cpu, sa = gemm_inputs.fp8_matrix(M, lda, 93)
+        B_cpu, sb = gemm_inputs.fp8_matrix(N, ldb, 94)
+        dt = hk.HK_DTYPE_FP8_E4M3
+    else:
+        A_cpu, B_cpu = _bf16(M, lda, "uniform", 93), _bf16(N, ldb, "uniform", 94)
+        sa = sb = 1.0
+        dt = hk.HK_DTYPE_BF16
+    A, B = A_cpu.cuda(), B_cpu.cuda()
+    need = hk.hk_gemm_workspace_size(dt, A, B, A, M, N, K, lda, ldb, N, repack="always")
+    rows = M if which == "A" else N
+    padded = (K * esz + 1023) // 1024 * 1024
+    padded += 1024 if padded % 8192 == 0 else 0
+    assert need == (rows * padded + 255) // 256 * 256, (need, rows, padded)
+    ws = _ws_tensor(need)
+    direct = _run(dt, A, B, M, N, K, lda, ldb, N, sa, sb, repack="never")
+    rep = _run(dt, A, B, M, N, K, lda, ldb, N, sa, sb, repack="always", workspace=ws)
+    assert torch.equal(direct.view(torch.int16), rep.view(torch.int16))
+    ref, S = oracle.gemm(dtype, gemm_inputs.bits(A_cpu).ravel(), gemm_inputs.bits(B_cpu).ravel(),
+                         M, N, K, lda=lda, ldb=ldb, scale_a=sa, scale_b=sb)
+    st = oracle.compare(_bits16(rep)[:M, :N], ref, S, rel_tol=RTOL)
+    _say("repack one operand", dtype, which, need, {k: st[k] for k in st if k != "ulp_hist"})
+    assert st["ok"], st
+
+
 def test_ragged_full_size_with_workspace():
     """The ragged MLP shape in the launch configuration the bench times for it:
     hk_gemm_ex with a workspace, which copies both operands (16 400-byte rows)
