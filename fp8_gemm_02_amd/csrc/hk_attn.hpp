@@ -574,7 +574,6 @@ __device__ __forceinline__ void attn_fwd_persist(const AttnArgs& g, HK_LDS uint8
         const HK_LDS uint8_t* kimg = lds + buf * 2u * kImgB;
         const HK_LDS uint8_t* vimg = kimg + kImgB;
         const int32_t k0 = j * kAttnKV;
-        auto prefetch_q = [&]() {};
 
         // a wave whose queries all lie before this block has nothing to add
         if (!kCausal || k0 <= q0w + 31) {
@@ -600,7 +599,6 @@ __device__ __forceinline__ void attn_fwd_persist(const AttnArgs& g, HK_LDS uint8
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            prefetch_q();
             // ---- masked scores (causal, or keys past N) become -inf, on a
             // separate path that blocks away from the edges skip
             const bool masked = (kCausal && k0 + kAttnKV - 1 > q0w) || k0 + kAttnKV > N;
@@ -682,8 +680,6 @@ __device__ __forceinline__ void attn_fwd_persist(const AttnArgs& g, HK_LDS uint8
                     o[db][0] = mfma_bf16_16x16x32(vf[db][c], pf[0][c], o[db][0]);
                     o[db][1] = mfma_bf16_16x16x32(vf[db][c], pf[1][c], o[db][1]);
                 }
-        } else {
-            prefetch_q();
         }
     }
 
