@@ -209,8 +209,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
         voff_k[i] = row * ktok_b + ((pc ^ attn_kswz<D>(row)) * 16u);
         voff_v[i] = row * vtok_b + ((pc ^ attn_vswz<D>(row)) * 16u);
     }
-    auto issue = [&](int32_t j) {
-        HK_LDS uint8_t* kimg = lds + (uint32_t)(j & 1) * 2u * kImgB;
+    // block j into buffer p (= j % 2)
+    auto issue = [&](int32_t j, uint32_t p) {
+        HK_LDS uint8_t* kimg = lds + p * 2u * kImgB;
         HK_LDS uint8_t* vimg = kimg + kImgB;
         const uint32_t kb = (uint32_t)j * kAttnKV;
 #pragma unroll
@@ -262,13 +263,16 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
     // One barrier per block: past it, block j has landed (every wave waited
     // for its own part) and every wave has finished block j - 1, whose
     // buffer then takes block j + 1.
-    if (nblk > 0) issue(0);
-    for (int32_t j = 0; j < nblk; ++j) {
+    if (nblk > 0) issue(0, 0u);
+    // The block loop runs unrolled by two, so that each block's buffer is a
+    // constant and its LDS reads take the buffer offset as an immediate.
+    auto block = [&](int32_t j, auto pc) {
+        constexpr uint32_t p = decltype(pc)::value;
         wait_vmcnt0();
         wait_lgkmcnt0();
         fenced_barrier();
-        if (j + 1 < nblk) issue(j + 1);
-        const HK_LDS uint8_t* kimg = lds + (uint32_t)(j & 1) * 2u * kImgB;
+        if (j + 1 < nblk) issue(j + 1, p ^ 1u);
+        const HK_LDS uint8_t* kimg = lds + p * 2u * kImgB;
         const HK_LDS uint8_t* vimg = kimg + kImgB;
         const int32_t k0 = j * kAttnKV;
 
@@ -377,7 +381,12 @@ __device__ __forceinline__ void attn_fwd_body(const AttnArgs& g, HK_LDS uint8_t*
                     o[db][1] = mfma_bf16_16x16x32(vf[db][c], pf[1][c], o[db][1]);
                 }
         }
+    };
+    for (int32_t j = 0; j < nblk; j += 2) {
+        block(j, std::integral_constant<uint32_t, 0>{});
+        if (j + 1 < nblk) block(j + 1, std::integral_constant<uint32_t, 1>{});
     }
+
 
     // ---- epilogue: O = O^T / l, LSE = (m + log2 l) ln 2
     uint16_t* Oh = g.O + (int64_t)b * g.so[0] + (int64_t)h * g.so[1];
