@@ -581,13 +581,17 @@ __device__ __forceinline__ void il4_bf16_body(const GemmArgs& g, const IL4Buf bu
         acc_settle();  // the zeroed accumulators before the first MFMA reads them
     };
 
-    // MFMA q of a slice: B block q % 8 as the "A" operand, A block q / 8 as
-    // the "B" operand (C^T, so a lane holds 4 consecutive columns of a C row).
-    // Fragments are read in the order the list consumes them: A block 0,
-    // B blocks 0-7, A blocks 1-7.
+    // MFMA q of a slice: A block mb = q / 8 as the "B" operand and B block nb
+    // as the "A" operand (C^T, so a lane holds 4 consecutive columns of a C
+    // row), nb running 0-7 on even rows and 7-0 on odd ones, so that every
+    // MFMA shares a fragment with the one before it (about 0.6 % faster than
+    // restarting each row at nb = 0: the chip is power-bound, and fewer
+    // operand reads leave it more clock).  Fragments are read in the order the
+    // list consumes them: A block 0, B blocks 0-7, A blocks 1-7.
     i32x4 fx[16], fy[16];
     auto mfma = [&](const i32x4 (&fr)[16], int q) {
-        const int mb = q >> 3, nb = q & 7;
+        const int mb = q >> 3;
+        const int nb = (mb & 1) ? 7 - (q & 7) : (q & 7);
         mfma_bf16_16x16x32_pinned(acc[mb][nb], fr[8 + nb], fr[mb]);
     };
     auto rd = [&](i32x4 (&fr)[16], const IL4Buf& d, int s, int r) {
@@ -963,7 +967,10 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
     auto slice0 = [&](auto masked, const IL4Buf& cur, uint32_t t) {
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
-            mfma(q >> 3, q & 7);
+            // rows of A blocks 0-3, B blocks reversed on odd rows (each MFMA
+            // shares a fragment with the one before it)
+            const int mb = q >> 3;
+            mfma(mb, (mb & 1) ? 7 - (q & 7) : (q & 7));
             if (q % 3 == 0 && q / 3 < 6) get_a(masked, cur, 2 + q / 3, t, seq);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -974,7 +981,11 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
                       const IL4Buf& nxt, uint32_t u1, uint32_t sq1, auto glob) {
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
-            mfma(4 + (q & 3), q >> 2);
+            // columns of B blocks 0-7 (ascending: each column's fragment is
+            // refilled for the next stage once consumed), A blocks 4-7
+            // reversed on odd columns
+            const int nb = q >> 2;
+            mfma(4 + ((nb & 1) ? 3 - (q & 3) : (q & 3)), nb);
             if (q & 1) send(masked, tt, cur, s, q >> 1, glob);
             else if ((q & 3) == 0 && q > 0) get_b(masked, nxt, (q >> 2) - 1, u1, sq1);
             else if (q == 2) get_a(masked, nxt, 0, u1, sq1);
