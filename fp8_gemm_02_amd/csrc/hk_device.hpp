@@ -19,6 +19,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Four dwords at a dword-aligned address: the vector memory unit takes a
+// 16-byte access at any dword alignment, so C rows whose start is only
+// 4-byte aligned (an even ldc) still get one store per 8 bf16.
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 #define HK_LDS __attribute__((address_space(3)))
 
@@ -294,12 +298,14 @@ __device__ __forceinline__ void swap_row_pairs(uint32_t& x, uint32_t& y) {
 
 // Store one 16-row block of a wave's C sub-tile.  Lane (r, g) (r = lane % 16,
 // g = lane / 16) holds, for blocks j = 0..kNB-1, C[m][c0 + 16j + 4g .. +3] in
-// a[j] (times s); m is the lane's row, ok whether it lies inside C.  With
-// 16-byte aligned 8-column groups (align 16) each pair of blocks (j, j+1)
-// goes out as one 16-byte store per lane: lane groups g and g+1 trade their
-// halves (swap_row_pairs), so that even groups hold columns
-// c0 + 16j + 4g .. +7 and odd groups c0 + 16(j+1) + 4(g-1) .. +7.  Half the
-// store instructions of 8-byte stores, each covering 64 bytes of a row.
+// a[j] (times s); m is the lane's row, ok whether it lies inside C.  Whenever
+// the 8-column groups are at least dword aligned (align 16, 8 or 4) each pair
+// of blocks (j, j+1) goes out as one 16-byte store per lane: lane groups g
+// and g+1 trade their halves (swap_row_pairs), so that even groups hold
+// columns c0 + 16j + 4g .. +7 and odd groups c0 + 16(j+1) + 4(g-1) .. +7.
+// Half the store instructions of 8-byte stores and a quarter of 4-byte ones,
+// each covering 64 bytes of a row.  c0 is a multiple of 16 columns, so every
+// group starts a multiple of 16 bytes into its row.
 template <int kNB>
 __device__ __forceinline__ void store_c_rows(uint16_t* crow, bool ok, int32_t c0, uint32_t g,
                                              int32_t N, const f32x4 (&a)[kNB], float s,
@@ -309,7 +315,7 @@ __device__ __forceinline__ void store_c_rows(uint16_t* crow, bool ok, int32_t c0
     // computed here, not hoisted out of the tile loop and kept live (spilled)
     // across it
     asm volatile("" : "+v"(g));
-    if (align >= 16) {
+    if (align >= 4) {
 #pragma unroll
         for (int j = 0; j < kNB; j += 2) {
             const f32x4 u = a[j] * s, v = a[j + 1] * s;
@@ -321,7 +327,8 @@ __device__ __forceinline__ void store_c_rows(uint16_t* crow, bool ok, int32_t c0
                                              : 16 * j + 4 * (int32_t)g);
             if (ok) {
                 if (c + 8 <= N) {
-                    *reinterpret_cast<uint4*>(crow + c) = make_uint4(x0, x1, y0, y1);
+                    const u32x4_a4 w = {x0, x1, y0, y1};
+                    *reinterpret_cast<u32x4_a4*>(crow + c) = w;
                 } else {
                     store_packed4(crow + c, c, N, x0, x1, align);
                     store_packed4(crow + c + 4, c + 4, N, y0, y1, align);

@@ -262,6 +262,46 @@ def test_sixteen_byte_stores_and_ragged_columns(dtype, N):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("ldc_extra,c_off", [(2, 0), (4, 0), (6, 0), (8, 2), (8, 4), (8, 6), (6, 2)])
+@pytest.mark.parametrize("N", [13, 264, 270])
+@pytest.mark.parametrize("schedule", ["interleave4", "pingpong8"])
+def test_sixteen_byte_stores_at_dword_alignment(dtype, ldc_extra, c_off, N, schedule):
+    """C rows that start only 4- or 8-byte aligned (an even ldc that is not a
+    multiple of 8, or C itself offset by 2, 4 or 6 elements): the 4-wave and
+    ping-pong kernels still store 8 columns per lane in one 16-byte store at dword
+    alignment.  Bit-exact; the columns past N, the elements before C and the
+    guard rows untouched."""
+    if schedule == "pingpong8" and N != 270:
+        pytest.skip("the ping-pong store path is covered at N = 270")
+    M, K = 290, 192
+    ldc = (N + 7) // 8 * 8 + ldc_extra
+    if dtype == "bf16":
+        A, B, sa, sb = _bf16(M, K, "int4", 75), _bf16(N, K, "int4", 76), 1.0, 1.0
+        dt = hk.HK_DTYPE_BF16
+    else:
+        A, _ = gemm_inputs.fp8_matrix(M, K, 77, integer=True)
+        B, _ = gemm_inputs.fp8_matrix(N, K, 78, integer=True)
+        sa, sb, dt = 2.0, 0.25, hk.HK_DTYPE_FP8_E4M3
+    guard = 2
+    Cbuf = torch.full(((M + 2 * guard) * ldc + 8,), SENTINEL, dtype=torch.int16,
+                      device="cuda").view(torch.bfloat16)
+    start = guard * ldc + c_off
+    Cv = Cbuf[start:]
+    assert Cv.data_ptr() % 4 == 0 and ldc % 2 == 0
+    assert Cv.data_ptr() % 16 != 0 or ldc % 8 != 0
+    _say("dword-aligned 16-byte stores", dtype, (M, N, K), "ldc", ldc, "offset", c_off)
+    _run(dt, A.cuda(), B.cuda(), M, N, K, K, K, ldc, sa, sb, C=Cv, schedule=schedule)
+    allb = _bits16(Cbuf)
+    assert (allb[:start] == SENTINEL).all() and (allb[start + M * ldc:] == SENTINEL).all()
+    body = allb[start:start + M * ldc].reshape(M, ldc)
+    assert (body[:, N:] == SENTINEL).all()
+    ref, _ = oracle.gemm(dtype, gemm_inputs.bits(A).ravel(), gemm_inputs.bits(B).ravel(), M, N, K,
+                         scale_a=sa, scale_b=sb)
+    st = oracle.compare(body[:, :N], ref, exact=True)
+    assert st["ok"], st
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_k_order_does_not_change_exact_results(dtype):
     """The 4-wave kernels walk K in a per-chiplet rotated order (chiplet
     w mod 8 starts w mod 8 eighths of the way in).  Changing the tile order
