@@ -67,7 +67,8 @@ class GemmOpts(ctypes.Structure):
                 ("layout_a", ctypes.c_int32), ("layout_b", ctypes.c_int32),
                 ("clock_stamps", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_int64), ("repack", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("scale_a_dev", ctypes.c_void_p),
+                ("scale_b_dev", ctypes.c_void_p)]
 
 
 class AttnStrides(ctypes.Structure):
@@ -152,7 +153,8 @@ def _stream(s) -> int:
 
 
 def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
-          clock_stamps=None, workspace=None, workspace_bytes=None, repack=0):
+          clock_stamps=None, workspace=None, workspace_bytes=None, repack=0,
+          scale_a_dev=None, scale_b_dev=None):
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
     if isinstance(grid_order, str):
@@ -169,6 +171,8 @@ def _opts(schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
             workspace.numel() * workspace.element_size()
     o.workspace_bytes = int(workspace_bytes)
     o.repack = REPACKS[repack] if isinstance(repack, str) else int(repack)
+    o.scale_a_dev = _ptr(scale_a_dev) or None
+    o.scale_b_dev = _ptr(scale_b_dev) or None
     return o
 
 
@@ -201,14 +205,16 @@ def hk_gemm_mxfp8(A, B, C, M, N, K, lda, ldb, ldc, scales_a, scales_b, ld_scales
 def hk_gemm_ex(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,
                schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
                stream=None, raise_on_error=True, clock_stamps=None, workspace=None,
-               workspace_bytes=None, repack=0):
+               workspace_bytes=None, repack=0, scale_a_dev=None, scale_b_dev=None):
     """clock_stamps: None, or a 16-byte aligned device buffer of 32 uint64 (a
     torch tensor or a pointer) for the launch's clock record.  workspace: None,
     or a 256-byte aligned device buffer (tensor: its size is taken; pointer:
     give workspace_bytes) for repacked operands; repack: "auto", "never",
-    "always" (or the HK_REPACK_* value)."""
+    "always" (or the HK_REPACK_* value).  scale_a_dev, scale_b_dev: None, or a
+    device fp32 (tensor or pointer) read when the kernel runs in place of
+    scale_a (scale_b); FP8 only."""
     o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b, clock_stamps,
-              workspace, workspace_bytes, repack)
+              workspace, workspace_bytes, repack, scale_a_dev, scale_b_dev)
     st = lib().hk_gemm_ex(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                           float(scale_a), float(scale_b), ctypes.byref(o), _stream(stream))
     return _check(st, "hk_gemm_ex", raise_on_error)
@@ -230,11 +236,12 @@ HK_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 def hk_gemm_ex_noalloc(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a=1.0, scale_b=1.0,
                        schedule=0, grid_order=0, group_m=0, window=0, layout_a=0, layout_b=0,
-                       stream=None, raise_on_error=True, clock_stamps=None, repack=0):
+                       stream=None, raise_on_error=True, clock_stamps=None, repack=0,
+                       scale_a_dev=None, scale_b_dev=None):
     """hk_gemm_ex with any repack workspace taken from the library's own device
     array (HK_NOALLOC_SCRATCH_BYTES per GPU): the call allocates nothing."""
     o = _opts(schedule, grid_order, group_m, window, layout_a, layout_b, clock_stamps,
-              repack=repack)
+              repack=repack, scale_a_dev=scale_a_dev, scale_b_dev=scale_b_dev)
     st = lib().hk_gemm_ex_noalloc(int(dtype), _ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                   float(scale_a), float(scale_b), ctypes.byref(o),
                                   _stream(stream))

@@ -13,7 +13,7 @@
 #include "hk_gemm.h"
 #include "hk_kernels.hpp"
 
-#define HK_VERSION 200  // 0.2.0
+#define HK_VERSION 300  // 0.3.0: device-resident FP8 scales
 
 // ------------------------------------------------------------------ kernels
 //
@@ -212,6 +212,12 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
             (opts->workspace == nullptr && opts->workspace_bytes != 0) ||
             !aligned(opts->workspace, 256))
             return HK_ERROR_INVALID_VALUE;
+        // scales read from device memory: FP8 per-tensor scales only
+        if ((opts->scale_a_dev != nullptr || opts->scale_b_dev != nullptr) &&
+            dtype != HK_DTYPE_FP8_E4M3)
+            return HK_ERROR_INVALID_VALUE;
+        if (!aligned(opts->scale_a_dev, 4) || !aligned(opts->scale_b_dev, 4))
+            return HK_ERROR_INVALID_VALUE;
     }
     if (M == 0 || N == 0) return HK_SUCCESS;
     if (C == nullptr || ldc < N || !aligned(C, 2)) return HK_ERROR_INVALID_VALUE;
@@ -228,8 +234,8 @@ hk_status validate(int32_t dtype, const void* A, const void* B, const void* C, i
 
 // Fills *p; assumes validate() passed and M, N > 0.
 hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, int64_t M,
-                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale,
-                    const hk_gemm_opts* opts, Plan* p) {
+                    int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale_a,
+                    float scale_b, const hk_gemm_opts* opts, Plan* p) {
     memset(p, 0, sizeof(*p));
     const int64_t esz = dtype == HK_DTYPE_BF16 ? 2 : 1;
     if (M > INT32_MAX - 512 || N > INT32_MAX - 512 || K > INT32_MAX / 2)
@@ -376,7 +382,14 @@ hk_status make_plan(int32_t dtype, const void* A, const void* B, const void* C, 
     g.lda_b = (uint32_t)lda_b;
     g.ldb_b = (uint32_t)ldb_b;
     g.ldc = ldc;
-    g.scale = (fp8 && !mx) ? scale : 1.0f;
+    g.scale_pa = opts ? opts->scale_a_dev : nullptr;
+    g.scale_pb = opts ? opts->scale_b_dev : nullptr;
+    // with one factor read on the device, g.scale carries the other
+    g.scale = !(fp8 && !mx)        ? 1.0f
+              : g.scale_pa && g.scale_pb ? 1.0f
+              : g.scale_pa       ? scale_b
+              : g.scale_pb       ? scale_a
+                                 : scale_a * scale_b;
     g.SA = nullptr;
     g.SB = nullptr;
     g.ldsa = g.ldsb = 0;
@@ -539,11 +552,14 @@ hk_status gemm_common(int32_t dtype, const void* A, const void* B, void* C, int6
     if (dtype == HK_DTYPE_MXFP8_E4M3) return HK_ERROR_INVALID_VALUE;
     hk_status s = validate(dtype, A, B, C, M, N, K, lda, ldb, ldc, opts);
     if (s != HK_SUCCESS) return s;
-    if (dtype == HK_DTYPE_FP8_E4M3 && (!isfinite(scale_a) || !isfinite(scale_b)))
+    // a by-value scale counts unless a device pointer replaces it
+    if (dtype == HK_DTYPE_FP8_E4M3 &&
+        ((!isfinite(scale_a) && !(opts && opts->scale_a_dev)) ||
+         (!isfinite(scale_b) && !(opts && opts->scale_b_dev))))
         return HK_ERROR_INVALID_VALUE;
     if (M == 0 || N == 0) return HK_SUCCESS;
     Plan p;
-    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a * scale_b, opts, &p);
+    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, scale_a, scale_b, opts, &p);
     if (s != HK_SUCCESS) return s;
     if (K == 0) return zero_c(C, M, N, ldc, stream);
     Repack rp;
@@ -568,7 +584,7 @@ hk_status gemm_common(int32_t dtype, const void* A, const void* B, void* C, int6
         ldb2 = rp.b_ld_b / esz;
     }
     Plan p2;
-    s = make_plan(dtype, A2, B2, C, M, N, K, lda2, ldb2, ldc, scale_a * scale_b, opts, &p2);
+    s = make_plan(dtype, A2, B2, C, M, N, K, lda2, ldb2, ldc, scale_a, scale_b, opts, &p2);
     if (s != HK_SUCCESS) return s;
     p2.args.stamps = p.args.stamps;
     return launch(p2, stream);
@@ -589,7 +605,8 @@ hk_status gemm_mx(const void* A, const void* B, void* C, int64_t M, int64_t N, i
             return HK_ERROR_NOT_SUPPORTED;
     }
     Plan p;
-    s = make_plan(HK_DTYPE_MXFP8_E4M3, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, nullptr, &p);
+    s = make_plan(HK_DTYPE_MXFP8_E4M3, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, 1.0f, nullptr,
+                  &p);
     if (s != HK_SUCCESS) return s;
     if (K == 0) return zero_c(C, M, N, ldc, stream);
     p.args.SA = (const uint8_t*)SA;
@@ -642,7 +659,7 @@ hk_status hk_gemm_plan(int32_t dtype, const void* A, const void* B, const void* 
     memset(out, 0, sizeof(*out));
     if (M == 0 || N == 0) return HK_SUCCESS;
     Plan p;
-    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, opts, &p);
+    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, 1.0f, opts, &p);
     if (s != HK_SUCCESS) return s;
     out->schedule = p.schedule;
     out->grid_order = p.grid_order;
@@ -670,7 +687,7 @@ hk_status hk_gemm_workspace_size(int32_t dtype, const void* A, const void* B, co
     if (s != HK_SUCCESS) return s;
     if (M == 0 || N == 0 || K == 0) return HK_SUCCESS;
     Plan p;
-    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, opts, &p);
+    s = make_plan(dtype, A, B, C, M, N, K, lda, ldb, ldc, 1.0f, 1.0f, opts, &p);
     if (s != HK_SUCCESS) return s;
     Repack rp;
     s = plan_repack(p, M, N, K, opts, INT64_MAX, &rp);

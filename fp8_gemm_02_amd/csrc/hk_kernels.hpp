@@ -42,7 +42,13 @@ struct GemmArgs {
     int32_t M, N, K;        // K in elements
     uint32_t lda_b, ldb_b;  // row strides of A and B in bytes
     int64_t ldc;            // row stride of C in elements
-    float scale;            // multiplies the fp32 accumulator (FP8 only)
+    // FP8 only (1 otherwise): the accumulator scale scale_a * scale_b, or,
+    // when exactly one factor comes from device memory, the other factor
+    float scale;
+    // FP8 only: NULL, or a device fp32 that replaces scale_a (scale_b), read
+    // when the kernel runs
+    const float* scale_pa;
+    const float* scale_pb;
     int32_t c_align;        // guaranteed alignment of 8-column (16) or 4-column groups of C (8, 4, 2)
     GridParams grid;
     // MXFP8 only: E8M0 scale bytes, one per 32 K-elements of a row
@@ -55,6 +61,16 @@ struct GemmArgs {
     // optional clock record (clock_stamp_begin); written by the persistent kernels only
     uint64_t* stamps;
 };
+
+// The FP8 accumulator scale: the host's fp32 product when both factors were
+// passed by value, else the same fp32 product with the device-resident
+// factors read now (equal values give the same bits either way).
+__device__ __forceinline__ float fp8_scale(const GemmArgs& g) {
+    if (g.scale_pa == nullptr && g.scale_pb == nullptr) return g.scale;
+    const float a = g.scale_pa != nullptr ? *g.scale_pa : g.scale;
+    const float b = g.scale_pb != nullptr ? *g.scale_pb : g.scale;
+    return a * b;
+}
 
 constexpr int kRowBytes = 128;  // bytes of K per stage in every tile row
 constexpr int kChunks = 8;      // 16-byte chunks per tile row per stage
@@ -357,11 +373,12 @@ __device__ __forceinline__ void pp8_body(const GemmArgs& g, const PP8Buf buf0, c
         // holds C[m][n..n+3] for each (mb, nb)
         const uint32_t le = lane_id_here();
         const int32_t mrow = cur.m0 + (int32_t)(grp * 128u + (le & 15u));
+        const float sc = kFp8 ? fp8_scale(g) : 1.0f;
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const int32_t m = mrow + mb * 16;
             store_c_rows(g.C + (int64_t)m * g.ldc, m < g.M, cur.n0 + (int32_t)(wq * 64u), le >> 4,
-                         g.N, acc[mb], kFp8 ? g.scale : 1.0f, g.c_align);
+                         g.N, acc[mb], sc, g.c_align);
         }
         if (w_next >= total) break;
         w = w_next;
@@ -1077,11 +1094,12 @@ __device__ __forceinline__ void il4_fp8_body(const GemmArgs& g, const IL4Buf buf
         // ---- epilogue: lane holds C[m][n..n+3] of block (mb, nb), times sA*sB
         const uint32_t le = lane_id_here();
         const int32_t mrow = cur.m0 + (int32_t)(arow + (le & 15u));
+        const float sc = fp8_scale(g);
 #pragma unroll
         for (int mb = 0; mb < 8; ++mb) {
             const int32_t m = mrow + mb * 16;
             store_c_rows(g.C + (int64_t)m * g.ldc, m < g.M, cur.n0 + (int32_t)brow, le >> 4, g.N,
-                         acc[mb], g.scale, g.c_align);
+                         acc[mb], sc, g.c_align);
         }
         if (w_next >= total) break;
         w = w_next;
@@ -1565,6 +1583,7 @@ __device__ __forceinline__ void st4_body(const GemmArgs& g, HK_LDS i32x4* ring) 
     // ---- epilogue: lane holds C[m][n..n+3] of block (mb, nb)
     const int32_t mrow = m0 + (int32_t)(arow + r16);
     const int32_t ncol = n0 + (int32_t)(brow + g4 * 4u);
+    const float sc = kFp8 ? fp8_scale(g) : 1.0f;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
         const int32_t m = mrow + mb * 16;
@@ -1575,7 +1594,7 @@ __device__ __forceinline__ void st4_body(const GemmArgs& g, HK_LDS i32x4* ring) 
                 const int32_t n = ncol + nb * 16;
                 if (n < g.N) {
                     f32x4 v = acc[mb][nb];
-                    if constexpr (kFp8) v *= g.scale;
+                    if constexpr (kFp8) v *= sc;
                     store_bf16x4(crow + n, n, g.N, v, g.c_align);
                 }
             }
@@ -1673,6 +1692,7 @@ __device__ __forceinline__ void basic_body(const GemmArgs& g, HK_LDS i32x4* sA, 
 
     const int32_t mrow = m0 + (int32_t)(wm * 32u + r16);
     const int32_t ncol = n0 + (int32_t)(wn * 32u + g4 * 4u);
+    const float sc = kFp8 ? fp8_scale(g) : 1.0f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         const int32_t m = mrow + mb * 16;
@@ -1683,7 +1703,7 @@ __device__ __forceinline__ void basic_body(const GemmArgs& g, HK_LDS i32x4* sA, 
                 const int32_t n = ncol + nb * 16;
                 if (n < g.N) {
                     f32x4 v = acc[mb][nb];
-                    if constexpr (kFp8) v *= g.scale;
+                    if constexpr (kFp8) v *= sc;
                     store_bf16x4(crow + n, n, g.N, v, g.c_align);
                 }
             }

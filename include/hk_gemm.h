@@ -190,6 +190,18 @@ typedef enum hk_repack {
  * and are not preserved; it must stay valid until the call's work has
  * completed on the stream, and two calls that may run at the same time need
  * two workspaces.
+ *
+ * scale_a_dev, scale_b_dev: NULL, or a caller-owned device fp32 (4-byte
+ * aligned) that the kernel reads when it runs, in stream order, in place of
+ * the by-value scale_a (scale_b).  FP8 per-tensor scales only: with BF16 a
+ * non-NULL pointer is HK_ERROR_INVALID_VALUE, as is a misaligned one.  For
+ * scales computed on the device (an amax reduction, delayed scaling) this
+ * needs no copy to the host, and a captured HIP graph reads the values
+ * current at each replay.  The product is s = a * b in fp32, the same
+ * rounding as for by-value scales, so equal values give bit-identical C.
+ * The host cannot check these values: a non-finite one makes C non-finite,
+ * where a non-finite by-value scale is HK_ERROR_INVALID_VALUE (a by-value
+ * scale that a pointer replaces is not checked).
  */
 typedef struct hk_gemm_opts {
     int32_t schedule;    /* hk_schedule */
@@ -203,6 +215,8 @@ typedef struct hk_gemm_opts {
     int64_t workspace_bytes; /* its size in bytes */
     int32_t repack;      /* hk_repack */
     int32_t reserved;    /* must be zero */
+    const float *scale_a_dev; /* NULL, or device fp32 read in place of scale_a */
+    const float *scale_b_dev; /* NULL, or device fp32 read in place of scale_b */
 } hk_gemm_opts;
 
 /* What a call with these arguments would launch (filled by hk_gemm_plan). */
@@ -257,8 +271,10 @@ hk_status hk_gemm_mxfp8(const void *A, const void *B, void *C,
                         hk_stream_t stream);
 
 /* BF16 or FP8 with explicit options (opts may be NULL = defaults).
- * scale_a and scale_b are ignored for BF16.  HK_DTYPE_MXFP8_E4M3 is
- * HK_ERROR_INVALID_VALUE here (it needs hk_gemm_mxfp8's scale arrays). */
+ * scale_a and scale_b are ignored for BF16; for FP8 either may instead be
+ * read from device memory (opts->scale_a_dev, scale_b_dev).
+ * HK_DTYPE_MXFP8_E4M3 is HK_ERROR_INVALID_VALUE here (it needs
+ * hk_gemm_mxfp8's scale arrays). */
 hk_status hk_gemm_ex(int32_t dtype,
                      const void *A, const void *B, void *C,
                      int64_t M, int64_t N, int64_t K,

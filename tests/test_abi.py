@@ -108,13 +108,14 @@ def test_ex_rejects_bad_dtype_and_options(L):
 def test_opts_struct_matches_the_header():
     text = open(HEADER).read()
     body = re.search(r"typedef struct hk_gemm_opts \{(.*?)\} hk_gemm_opts;", text, re.S).group(1)
-    fields = re.findall(r"(int32_t|int64_t|uint64_t \*|void \*)\s*(\w+);", body)
+    fields = re.findall(r"(int32_t|int64_t|uint64_t \*|const float \*|void \*)\s*(\w+);", body)
     ctype = {"int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "uint64_t *": ctypes.c_void_p,
-             "void *": ctypes.c_void_p}
+             "void *": ctypes.c_void_p, "const float *": ctypes.c_void_p}
     assert [(n, ctype[t]) for t, n in fields] == list(hk.GemmOpts._fields_)
-    assert ctypes.sizeof(hk.GemmOpts) == 56
+    assert ctypes.sizeof(hk.GemmOpts) == 72
     assert hk.GemmOpts.clock_stamps.offset == 24 and hk.GemmOpts.workspace.offset == 32
     assert hk.GemmOpts.workspace_bytes.offset == 40 and hk.GemmOpts.repack.offset == 48
+    assert hk.GemmOpts.scale_a_dev.offset == 56 and hk.GemmOpts.scale_b_dev.offset == 64
 
 
 def test_chiplet_clocks_from_a_record():
@@ -463,6 +464,34 @@ def test_repack_options_are_validated(L):
     o = hk._opts(repack="always")
     st = L.hk_gemm_ex(0, FAKE, FAKE, FAKE, 32, 32, 64, 72, 64, 32, 1.0, 1.0, ctypes.byref(o), None)
     assert st == hk.HK_ERROR_INVALID_VALUE
+
+
+def test_device_scale_pointers_are_validated(L):
+    """Device-resident scales are for per-tensor FP8 only and must be dword
+    aligned; both are checked before any HIP call."""
+    def ex(dtype, **f):
+        o = hk.GemmOpts()
+        for k, v in f.items():
+            setattr(o, k, v)
+        return L.hk_gemm_ex(dtype, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0, 1.0,
+                            ctypes.byref(o), None)
+    for field in ("scale_a_dev", "scale_b_dev"):
+        assert ex(hk.HK_DTYPE_BF16, **{field: FAKE}) == hk.HK_ERROR_INVALID_VALUE, field
+        assert ex(hk.HK_DTYPE_MXFP8_E4M3, **{field: FAKE}) == hk.HK_ERROR_INVALID_VALUE, field
+        for off in (1, 2, 3):
+            st = ex(hk.HK_DTYPE_FP8_E4M3, **{field: FAKE + off})
+            assert st == hk.HK_ERROR_INVALID_VALUE, (field, off)
+    # a non-finite by-value scale with no pointer to replace it is still rejected
+    o = hk.GemmOpts()
+    o.scale_a_dev = FAKE
+    st = L.hk_gemm_ex(hk.HK_DTYPE_FP8_E4M3, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32, 1.0,
+                      float("nan"), ctypes.byref(o), None)
+    assert st == hk.HK_ERROR_INVALID_VALUE
+    # the plan (validation only) accepts aligned FP8 pointers
+    o = hk._opts(scale_a_dev=FAKE, scale_b_dev=FAKE + 4)
+    info = hk.PlanInfo()
+    assert L.hk_gemm_plan(hk.HK_DTYPE_FP8_E4M3, FAKE, FAKE, FAKE, 32, 32, 64, 64, 64, 32,
+                          ctypes.byref(o), ctypes.byref(info)) == hk.HK_SUCCESS
 
 
 def _ws(M, N, K, lda, ldb, dtype=0, **opts):
