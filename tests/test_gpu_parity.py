@@ -111,13 +111,16 @@ def test_fp8_ragged_full(M, N, K, integer):
     _full_check("fp8", A, B, M, N, K, K, K, exact=integer, sa=sa, sb=sb)
 
 
-@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "smalltile", "basic",
-                                      "interleave8", "producer_consumer"])
+# interleave8 and producer_consumer exist for BF16 only
+_SCHEDULES_BY_DTYPE = [(d, s) for d in ("bf16", "fp8")
+                       for s in ("pingpong8", "interleave4", "smalltile", "basic", "interleave8",
+                                 "producer_consumer")
+                       if d == "bf16" or s not in ("interleave8", "producer_consumer")]
+
+
+@pytest.mark.parametrize("dtype,schedule", _SCHEDULES_BY_DTYPE)
 @pytest.mark.parametrize("grid_order", ["row_major", "xcd"])
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_every_variant(schedule, grid_order, dtype):
-    if schedule in ("interleave8", "producer_consumer") and dtype == "fp8":
-        pytest.skip("BF16-only schedule")
     M, N, K = 777, 1029, 512
     if dtype == "bf16":
         A, B, sa, sb = _bf16(M, K, "normal", 11), _bf16(N, K, "normal", 12), 1.0, 1.0
@@ -128,14 +131,10 @@ def test_every_variant(schedule, grid_order, dtype):
                 grid_order=grid_order)
 
 
-@pytest.mark.parametrize("schedule", ["pingpong8", "interleave4", "interleave8", "smalltile",
-                                      "producer_consumer"])
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype,schedule", [(d, s) for d, s in _SCHEDULES_BY_DTYPE if s != "basic"])
 @pytest.mark.parametrize("M,N,K", [(513, 769, 1040), (256, 256, 128), (300, 40, 16)])
 def test_fast_schedules_ragged_integer(schedule, dtype, M, N, K):
     """Bit-exact on integer-valued inputs: edge tiles, K tails and odd stage counts."""
-    if schedule in ("interleave8", "producer_consumer") and dtype == "fp8":
-        pytest.skip("BF16-only schedule")
     if dtype == "bf16":
         A, B, sa, sb = _bf16(M, K, "int4", M + 3), _bf16(N, K, "int4", N + 4), 1.0, 1.0
     else:
@@ -263,16 +262,14 @@ def test_sixteen_byte_stores_and_ragged_columns(dtype, N):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("ldc_extra,c_off", [(2, 0), (4, 0), (6, 0), (8, 2), (8, 4), (8, 6), (6, 2)])
-@pytest.mark.parametrize("N", [13, 264, 270])
-@pytest.mark.parametrize("schedule", ["interleave4", "pingpong8"])
+@pytest.mark.parametrize("N,schedule", [(13, "interleave4"), (264, "interleave4"),
+                                        (270, "interleave4"), (270, "pingpong8")])
 def test_sixteen_byte_stores_at_dword_alignment(dtype, ldc_extra, c_off, N, schedule):
     """C rows that start only 4- or 8-byte aligned (an even ldc that is not a
     multiple of 8, or C itself offset by 2, 4 or 6 elements): the 4-wave and
     ping-pong kernels still store 8 columns per lane in one 16-byte store at dword
     alignment.  Bit-exact; the columns past N, the elements before C and the
     guard rows untouched."""
-    if schedule == "pingpong8" and N != 270:
-        pytest.skip("the ping-pong store path is covered at N = 270")
     M, K = 290, 192
     ldc = (N + 7) // 8 * 8 + ldc_extra
     if dtype == "bf16":
