@@ -142,7 +142,8 @@ def cpu_baseline(w, x, seconds: float):
                         scale_a=x["scale_a"], scale_b=x["scale_b"], threads=threads, want_s=False)
         return time.perf_counter() - t0
 
-    rows = max(1, threads // 2)
+    # calibration: one row per thread, so that the estimate sees every thread busy
+    rows = max(1, threads)
     t = run(rows)
     per_row = t / rows
     rows = int(max(threads, min(w.M, seconds / max(per_row, 1e-9))))
